@@ -1,0 +1,258 @@
+"""Pins of the oracle's mask construction against what the pages and plain
+counting fix (no GPU)."""
+
+import itertools
+import random
+
+import numpy as np
+import pytest
+
+from oracle import block_mask as bm
+from oracle import rng
+from long_context_sparse_block_amd import workloads as wl
+from tests.conftest import golden_path
+
+
+def _spec(nb, **kw):
+    s = dict(num_blocks=nb, num_groups=1, causal=False, win_before=0, win_after=0,
+             win_clamp=False, global_blocks=[], num_random=0, random_blocks=None,
+             literal_mode="none", literal_flags=None, literal_p=0.0, seed=0)
+    s.update(kw)
+    return s
+
+
+# ---------------------------------------------------------------- RNG ----
+
+def test_splitmix64_known_answers():
+    vals = [int(x, 16) for x in open(golden_path("splitmix64_seed0.txt"))
+            if x.strip() and not x.startswith("#")]
+    got = [rng.splitmix64((n * rng.GOLDEN_GAMMA) & rng.MASK64) for n in range(len(vals))]
+    assert got == vals
+
+
+def test_uniform_below_range_and_balance():
+    n = 7
+    counts = [0] * n
+    for k in range(7000):
+        c = rng.uniform_below(rng.draw_key(11, 2, 0, 0, k), n)
+        assert 0 <= c < n
+        counts[c] += 1
+    # each bin 1000 +- a generous 5 sigma
+    assert all(abs(x - 1000) < 5 * 30 for x in counts)
+
+
+def test_bernoulli_threshold_edges():
+    assert rng.bernoulli_threshold(0.0) == 0
+    assert rng.bernoulli_threshold(0.25) == 1 << 30
+    assert rng.bernoulli_threshold(1.0) == 1 << 32
+    assert rng.bernoulli_threshold(0.15) == 644245094  # floor(0.15 * 2^32)
+    rate = np.mean([rng.literal_flag(5, 0, j, 0.15) for j in range(20000)])
+    assert abs(rate - 0.15) < 0.01
+
+
+@pytest.mark.parametrize("n,r", [(1, 3), (2, 3), (5, 3), (64, 3), (100, 6), (3, 1)])
+def test_random_blocks_distinct_in_range(n, r):
+    for row in range(20):
+        d = rng.random_blocks(3, 0, row, n, r)
+        assert len(d) == min(r, n)
+        assert len(set(d)) == len(d)
+        assert all(0 <= x < n for x in d)
+    assert rng.random_blocks(3, 0, 0, 0, 3) == []
+
+
+# ------------------------------------------------ worked example (page) ----
+
+def _read_worked():
+    flags, w, rows = None, None, {"full": {}, "causal": {}}
+    for line in open(golden_path("compression_mask_worked.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("flags"):
+            flags = [int(x) for x in line.split()[1:]]
+        elif line.startswith("w "):
+            w = int(line.split()[1])
+        else:
+            kind, rest = line.split(" ", 1)
+            i, cols = rest.split(":")
+            rows[kind][int(i)] = [int(x) for x in cols.split()]
+    return flags, w, rows
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_compression_mask_worked_example(causal):
+    flags, w, rows = _read_worked()
+    nb = len(flags)
+    spec = _spec(nb, causal=causal, win_before=w, win_after=0 if causal else w,
+                 literal_mode="pair", literal_flags=np.array([flags], dtype=np.uint8))
+    row_ptr, col_idx, _ = bm.build(spec)
+    want = rows["causal" if causal else "full"]
+    for i in range(nb):
+        assert list(col_idx[row_ptr[i]:row_ptr[i + 1]]) == want[i]
+
+
+# ------------------------------------------- BigBird component counts ----
+
+@pytest.mark.parametrize("nb,wb,wa,globals_,r", [
+    (64, 1, 1, [0, 63], 3),      # the BigBird workload: 192 + 252 + 192 = 636
+    (32, 2, 2, [5], 4),
+    (40, 0, 3, [0, 1, 2], 1),
+    (17, 3, 1, [16], 5),
+])
+def test_bigbird_edge_count_formula(nb, wb, wa, globals_, r):
+    spec = _spec(nb, win_before=wb, win_after=wa, win_clamp=True,
+                 global_blocks=globals_, num_random=r, seed=9)
+    comp = bm.components(spec, 0)
+    w, g = wb + wa + 1, len(globals_)
+    assert comp["window"].sum() == nb * w
+    assert comp["global"].sum() == 2 * g * nb - g * g
+    assert comp["random"].sum() == nb * r
+    total = comp["window"].sum() + comp["global"].sum() + comp["random"].sum()
+    assert total == bm.bigbird_edge_count(nb, w, g, r)
+    if (nb, wb, wa, r) == (64, 1, 1, 3):
+        assert total == 636
+
+
+@pytest.mark.parametrize("nb,wb,gpre,r", [(8, 1, 1, 1), (128, 3, 0, 0), (512, 2, 4, 0), (50, 4, 3, 2)])
+def test_causal_component_closed_forms(nb, wb, gpre, r):
+    spec = _spec(nb, causal=True, win_before=wb, global_blocks=list(range(gpre)),
+                 num_random=r, seed=4)
+    comp = bm.components(spec, 0)
+    assert comp["window"].sum() == nb * (wb + 1) - wb * (wb + 1) // 2
+    assert comp["global"].sum() == gpre * nb - gpre * (gpre - 1) // 2
+    assert comp["random"].sum() == sum(min(r, i) for i in range(nb))
+
+
+def test_workload_component_numbers():
+    # tiny-fp32: window 15, prefix global 8, random 7 (stated in closed form)
+    s1 = wl.mask_spec(wl.BLOCK_WORKLOADS["tiny-fp32"])
+    c = bm.components(s1, 0)
+    assert (c["window"].sum(), c["global"].sum(), c["random"].sum()) == (15, 8, 7)
+    s5 = wl.mask_spec(wl.BLOCK_WORKLOADS["long-context"])
+    c = bm.components(s5, 0)
+    assert c["window"].sum() == 1533 and c["global"].sum() == 2042
+    s2 = wl.mask_spec(wl.BLOCK_WORKLOADS["compression-guided"])
+    c = bm.components(s2, 0)
+    assert c["window"].sum() == 506
+
+
+# ---------------------------------------------- union vs brute force ----
+
+def _brute_rows(spec):
+    """Every (g, i, j) decided by the textual definitions, one pair at a time."""
+    nb, G = spec["num_blocks"], spec["num_groups"]
+    causal = spec["causal"]
+    wb, wa = spec["win_before"], spec["win_after"]
+    flags = bm.literal_flags(spec)
+    rows = []
+    for g in range(G):
+        for i in range(nb):
+            if spec["num_random"] > 0:
+                if spec.get("random_blocks") is not None:
+                    n = i if causal else nb
+                    rnd = {int(x) for x in np.asarray(spec["random_blocks"])[g, i] if 0 <= int(x) < n}
+                else:
+                    rnd = set(rng.random_blocks(spec["seed"], g, i, i if causal else nb, spec["num_random"]))
+            else:
+                rnd = set()
+            row = []
+            for j in range(nb):
+                if causal and j > i:
+                    continue
+                if causal:
+                    inwin = i - wb <= j <= i
+                elif spec["win_clamp"]:
+                    width = wb + wa + 1
+                    if width >= nb:
+                        inwin = True
+                    else:
+                        start = min(max(i - wb, 0), nb - width)
+                        inwin = start <= j < start + width
+                else:
+                    inwin = i - wb <= j <= i + wa
+                glob = (i in spec["global_blocks"]) or (j in spec["global_blocks"])
+                outside = j < i - wb or j > i + wa
+                mode = spec["literal_mode"]
+                lit = (mode == "pair" and flags[g][i] and flags[g][j] and outside) or \
+                      (mode == "anyq" and flags[g][j] and outside)
+                if i == j or inwin or glob or (j in rnd) or lit:
+                    row.append(j)
+            rows.append(row)
+    return rows
+
+
+def _random_spec(seed):
+    R = random.Random(seed)
+    nb = R.randint(1, 40)
+    causal = R.random() < 0.5
+    wb = R.randint(0, 4)
+    wa = 0 if causal else R.randint(0, 3)
+    g = R.sample(range(nb), R.randint(0, min(3, nb)))
+    spec = _spec(nb, num_groups=R.randint(1, 3), causal=causal, win_before=wb, win_after=wa,
+                 win_clamp=R.random() < 0.5, global_blocks=sorted(g),
+                 num_random=R.randint(0, 4), literal_mode=R.choice(bm.LITERAL_MODES),
+                 literal_p=R.random(), seed=R.randint(0, 2**40))
+    if R.random() < 0.3 and spec["num_random"] > 0:
+        spec["random_blocks"] = wl.random_draws(spec["num_groups"], nb, spec["num_random"],
+                                                causal, seed).numpy()
+    return spec
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_union_matches_brute_force(seed):
+    spec = _random_spec(seed)
+    row_ptr, col_idx, sched = bm.build(spec)
+    rows = _brute_rows(spec)
+    assert row_ptr[0] == 0 and len(row_ptr) == len(rows) + 1
+    for r, want in enumerate(rows):
+        assert list(col_idx[row_ptr[r]:row_ptr[r + 1]]) == want
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_union_inclusion_exclusion(seed):
+    spec = _random_spec(100 + seed)
+    for g in range(spec["num_groups"]):
+        comp = bm.components(spec, g)
+        sets = [c & (np.tril(np.ones_like(c)) if spec["causal"] else True) for c in comp.values()]
+        ie = 0
+        for k in range(1, len(sets) + 1):
+            for combo in itertools.combinations(sets, k):
+                inter = np.logical_and.reduce(combo)
+                ie += (-1) ** (k + 1) * int(inter.sum())
+        assert ie == int(bm.block_mask(spec)[g].sum())
+
+
+def test_literal_pair_count():
+    flags = np.array([[1, 1, 0, 1, 0, 1, 1, 0, 0, 1, 1, 1]], dtype=np.uint8)
+    w = 2
+    spec = _spec(12, causal=True, win_before=w, literal_mode="pair", literal_flags=flags)
+    lit = bm.components(spec, 0)["literal"]
+    brute = sum(1 for i in range(12) for j in range(12)
+                if flags[0, i] and flags[0, j] and j < i - w)
+    assert lit.sum() == brute
+
+
+def test_schedule_is_longest_first_permutation():
+    spec = _random_spec(7)
+    spec["num_groups"] = 2
+    spec["random_blocks"] = None
+    row_ptr, col_idx, sched = bm.build(spec)
+    nb = spec["num_blocks"]
+    cnt = np.diff(row_ptr).reshape(2, nb)
+    for g in range(2):
+        assert sorted(sched[g]) == list(range(nb))
+        keys = [(-cnt[g, i], i) for i in sched[g]]
+        assert keys == sorted(keys)
+
+
+def test_workload_masks_well_formed():
+    for name in ("tiny-fp32", "compression-guided", "bigbird"):
+        spec = wl.mask_spec(wl.BLOCK_WORKLOADS[name])
+        row_ptr, col_idx, _ = bm.build(spec)
+        nb = spec["num_blocks"]
+        for r in range(len(row_ptr) - 1):
+            cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+            assert np.all(np.diff(cols) > 0)
+            assert (r % nb) in cols  # identity always present
+            if spec["causal"]:
+                assert cols.max() <= r % nb
