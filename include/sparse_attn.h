@@ -1,0 +1,213 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) sparse attention library.
+ *
+ * Three operations, all forward, all launched asynchronously on the caller's
+ * HIP stream:
+ *
+ *   sparse_attn_build_mask   block mask -> CSR key-block lists on the device
+ *   sparse_attn_fwd          block-sparse attention over a CSR mask
+ *   offset_attn_fwd          token-level attention over a table of distances
+ *
+ * and two host helpers (sparse_attn_mask_capacity, offset_attn_make_table).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless documented as HOST.
+ *  - The caller owns all memory.  The library never allocates, frees or
+ *    synchronises; every kernel goes on `stream` (NULL = the null stream).
+ *  - Argument errors are detected on the host before anything is launched and
+ *    nothing is written.  A failed launch returns SA_ERR_HIP and
+ *    sa_last_hip_error() describes it (thread-local text).  The library never
+ *    prints and never aborts.
+ *  - Tensors are [B, H, N, d] (K and V: [B, H_kv, N, d]) with d contiguous.
+ *    `strides` (HOST, may be NULL) gives for q, k, v, o in that order the
+ *    batch, head and sequence strides in ELEMENTS (int64 [4][3]); NULL means
+ *    contiguous.  Rows must be 16-byte aligned: every stride must be a
+ *    multiple of 8 elements (bf16) or 4 elements (fp32), and base pointers
+ *    16-byte aligned.
+ *  - Head h reads K/V head h / (H / H_kv) (grouped-query attention).
+ *  - lse is fp32 [B, H, N], contiguous, natural-log log-sum-exp of the scaled
+ *    logits of each query row; a query with no allowed key gets o = 0 and
+ *    lse = -inf.
+ *  - O is written in the input dtype, rounded to nearest even.
+ *  - Thread safety: the library keeps no state besides the thread-local error
+ *    text; calls are reentrant.  Calls that write the same buffers race.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sa_status;
+enum {
+  SA_OK = 0,
+  SA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  SA_ERR_INVALID = -2,     /* a size, stride, flag or list is out of range     */
+  SA_ERR_UNSUPPORTED = -3, /* valid, but outside the compiled kernel set       */
+  SA_ERR_CAPACITY = -4,    /* an output buffer is smaller than required        */
+  SA_ERR_HIP = -5          /* the HIP runtime reported an error                */
+};
+
+enum { SA_F32 = 0, SA_BF16 = 1 };
+
+/* Long-range "literal" component of the block mask. */
+enum {
+  SA_LIT_NONE = 0,
+  SA_LIT_PAIR = 1, /* row i attends literal block j iff l_i = l_j = 1 (both literal) */
+  SA_LIT_ANYQ = 2  /* row i attends every literal block j (query flag ignored)      */
+};
+
+#define SA_MAX_GLOBAL 64   /* global blocks per mask                       */
+#define SA_MAX_RANDOM 32   /* random blocks per row                        */
+#define SA_MAX_BLOCKS 16384 /* blocks per sequence (num_blocks)            */
+#define SA_MAX_OFFSETS 128 /* distances per offset table                   */
+
+/*
+ * Block mask description (HOST struct, passed by host pointer).
+ *
+ * Row i of group g lists, ascending and without repeats, the key blocks j of
+ *
+ *    I    {i}                        -- "Parameter-free Adaptive Sparse
+ *                                       Attention via Compression-Based Content
+ *                                       Selection", Sec. 3.2 Eq. 3
+ *    W    local window:  causal  {j : i - win_before <= j <= i}
+ *                        non-causal, win_clamp = 0: [i - win_before, i + win_after]
+ *                        non-causal, win_clamp = 1: the same width shifted inside
+ *                           [0, num_blocks) so every row keeps exactly
+ *                           win_before + win_after + 1 blocks ("BigBird" Sec. 2,
+ *                           |G_W| = N w)
+ *    G    global: every row attends the global blocks, a global row attends
+ *         every block ("BigBird" Sec. 2, |G_G| = 2gN - g^2)
+ *    R    num_random distinct uniform draws ("BigBird" Sec. 2, |G_R| = N r),
+ *         from [0, i) when causal (earlier blocks only) else [0, num_blocks)
+ *    L    literal blocks outside the window band [i - win_before, i + win_after]
+ *         (compression paper Sec. 3.2, M^lit), per literal_mode
+ *
+ * intersected with j <= i when causal.
+ *
+ * Random draws: `random_blocks` (DEVICE int32 [G][num_blocks][num_random]) gives
+ * them explicitly; entries outside the allowed range are ignored and repeats
+ * count once.  If NULL they are drawn with the library's counter-based
+ * SplitMix64 scheme keyed by (seed, 2, g, i, k): candidate k is
+ * ((key >> 32) * n) >> 32, repeats skipped, stop at min(r, n) values or 64 r
+ * candidates.
+ *
+ * Literal flags: `literal_flags` (DEVICE uint8 [G][num_blocks], nonzero =
+ * literal) gives them explicitly; if NULL, block j of group g is literal iff
+ * (key(seed, 1, g, j, 0) >> 32) < floor(literal_p * 2^32).
+ * key(seed, t, a, b, c) = sm(sm(sm(sm(sm(seed) ^ t) ^ a) ^ b) ^ c) with sm the
+ * SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).
+ */
+typedef struct sa_mask_desc {
+  int32_t num_blocks;           /* N_b = N / block, 1..SA_MAX_BLOCKS              */
+  int32_t num_groups;           /* G >= 1 independent masks                        */
+  int32_t causal;               /* 0 or 1                                          */
+  int32_t win_before;           /* >= 0                                            */
+  int32_t win_after;            /* >= 0; must be 0 when causal                     */
+  int32_t win_clamp;            /* 0 or 1 (non-causal only)                        */
+  const int32_t* global_blocks; /* HOST, ascending, unique, in [0, N_b); NULL if 0 */
+  int32_t num_global;           /* 0..SA_MAX_GLOBAL                                */
+  int32_t num_random;           /* 0..SA_MAX_RANDOM                                */
+  const int32_t* random_blocks; /* DEVICE [G][N_b][num_random] or NULL             */
+  int32_t literal_mode;         /* SA_LIT_*                                        */
+  const uint8_t* literal_flags; /* DEVICE [G][N_b] or NULL                         */
+  double literal_p;             /* in [0, 1]; used when literal_flags is NULL      */
+  uint64_t seed;
+} sa_mask_desc;
+
+/* Upper bound on the number of CSR entries the mask can have:
+ * G * N_b * (N_b + 1) / 2 when causal, G * N_b * N_b otherwise.
+ * Returns a negative sa_status if the description is invalid. */
+int64_t sparse_attn_mask_capacity(const sa_mask_desc* desc);
+
+/* Check a mask description without launching anything. */
+sa_status sparse_attn_check_mask_desc(const sa_mask_desc* desc);
+
+/*
+ * Build the CSR form of the mask on the device.
+ *   row_ptr  DEVICE int32 [G * N_b + 1]: row (g, i) is entries
+ *            [row_ptr[g*N_b + i], row_ptr[g*N_b + i + 1]) of col_idx.
+ *   col_idx  DEVICE int32 [col_capacity]; col_capacity must be at least
+ *            sparse_attn_mask_capacity(desc) (SA_ERR_CAPACITY otherwise).
+ *   sched    DEVICE int32 [G][N_b] or NULL: per group, the row ids ordered by
+ *            decreasing row length, ties by increasing row id (a longest-first
+ *            launch order for sparse_attn_fwd).
+ * Three kernels (count, prefix sum, fill) on `stream`; the result is unique
+ * (bit-exact for a given description).
+ */
+sa_status sparse_attn_build_mask(const sa_mask_desc* desc, int32_t* row_ptr, int32_t* col_idx,
+                                 int64_t col_capacity, int32_t* sched, hipStream_t stream);
+
+/*
+ * Block-sparse attention forward.
+ *
+ * For token t in query block qb = t / block of (b, h), with mask row
+ * r = g * N_b + qb, g = b * mask_batch_stride + h * mask_head_stride:
+ *   K(t) = tokens of the key blocks col_idx[row_ptr[r] .. row_ptr[r+1]),
+ *          restricted to s <= t when causal (the diagonal block is partially
+ *          masked; blocks after the query block contribute nothing);
+ *   o_t  = softmax_s(scale * <q_t, k_s>) . v_s over s in K(t);
+ *   lse_t = ln sum_s exp(scale * <q_t, k_s>).
+ * This is the block mask expanded to tokens and ANDed with the causal triangle
+ * (compression paper Sec. 3.4 and Appendix B Algorithm 1 step 4), evaluated
+ * without materialising it.
+ *
+ *   dtype      SA_BF16 (MFMA path) or SA_F32
+ *   d, block   each 64 or 128; N % block == 0
+ *   row_ptr/col_idx  as built by sparse_attn_build_mask (any canonical CSR:
+ *              rows ascending and unique).  Column ids outside [0, N_b) are
+ *              skipped; entries beyond col_capacity are never read.
+ *   sched      DEVICE int32 [num_groups][N_b] launch order or NULL.
+ *   num_groups G; (B-1)*mask_batch_stride + (H-1)*mask_head_stride < G,
+ *              strides >= 0.
+ *   scale      logit scale, e.g. 1/sqrt(d)
+ */
+sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                          float* lse, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                          int32_t block, const int64_t* strides, const int32_t* row_ptr,
+                          const int32_t* col_idx, int64_t col_capacity, const int32_t* sched,
+                          int32_t num_groups, int64_t mask_batch_stride, int64_t mask_head_stride,
+                          int32_t causal, float scale, hipStream_t stream);
+
+/*
+ * Offset table of "Depth-Staggered Fibonacci Spacing for Sparse Attention",
+ * Sec. 2 ("Attended set"): the distinct distances
+ *   {0, 1, ..., W}  U  {floor(alpha * base[k] + 1/2) : k < K}
+ * that lie in [0, N), ascending.  Host only.
+ *   base       HOST int64 [K], each >= 0 (e.g. 1, 2, 3, 5, 8, ... below N)
+ *   table_out  HOST int32 [capacity]; count_out HOST int32 receives the size.
+ * SA_ERR_CAPACITY if the table does not fit (nothing written).
+ */
+sa_status offset_attn_make_table(int32_t W, double alpha, const int64_t* base, int32_t K, int32_t N,
+                                 int32_t* table_out, int32_t capacity, int32_t* count_out);
+
+/*
+ * Offset attention forward: query t attends keys {t - delta : delta in
+ * offsets, t - delta >= 0} (same page, Sec. 2: shifted gathers shared by all
+ * queries; the self distance 0 keeps every key set non-empty).
+ *   offsets    HOST int32 [num_offsets], ascending, unique, 0 <= delta < N,
+ *              1 <= num_offsets <= SA_MAX_OFFSETS
+ *   dtype      SA_BF16 or SA_F32; d 64 or 128; any N >= 1
+ */
+sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                          float* lse, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                          const int64_t* strides, const int32_t* offsets, int32_t num_offsets,
+                          float scale, hipStream_t stream);
+
+const char* sa_status_string(sa_status s);
+const char* sa_last_hip_error(void);
+int32_t sa_version(void);
+
+/* Layout of sa_mask_desc for bindings: writes min(n, 15) values -- sizeof,
+ * then the offset of each field in declaration order -- and returns 15. */
+int32_t sa_mask_desc_layout(int64_t* out, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,18 @@
+"""MI355X (gfx950) sparse block / offset attention: HIP kernels behind a C ABI.
+
+The library (lib/libsparse_attn.so, built by ``build.py``) exports
+sparse_attn_build_mask, sparse_attn_fwd and offset_attn_fwd; ``api`` binds them
+for PyTorch tensors.  ``workloads`` holds the seeded synthetic inputs.
+"""
+
+from .api import (  # noqa: F401
+    BlockMask,
+    SparseAttnError,
+    fibonacci_base,
+    offset_attn_fwd,
+    offset_attn_make_table,
+    sparse_attn_build_mask,
+    sparse_attn_check_mask_desc,
+    sparse_attn_fwd,
+    sparse_attn_mask_capacity,
+)

@@ -1,0 +1,198 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Tensors come from PyTorch (device memory and the current HIP stream); every
+step of the computation runs in the library's HIP kernels.  The functions keep
+the names of the C entry points.
+"""
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+_LIT_MODES = {"none": L.SA_LIT_NONE, "pair": L.SA_LIT_PAIR, "anyq": L.SA_LIT_ANYQ}
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        text = L.status_string(status)
+        if status == L.SA_ERR_HIP:
+            text += ": " + L.last_hip_error()
+        super().__init__(f"{what}: {text} ({status})")
+
+
+def _check(status, what):
+    if status != L.SA_OK:
+        raise SparseAttnError(status, what)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+@dataclass
+class BlockMask:
+    """CSR key-block lists on the device (see sparse_attn_build_mask)."""
+    row_ptr: torch.Tensor   # int32 [G * N_b + 1]
+    col_idx: torch.Tensor   # int32 [capacity]
+    sched: torch.Tensor     # int32 [G, N_b] or None
+    num_groups: int
+    num_blocks: int
+    causal: bool
+
+
+def _mask_desc(spec, device, keep):
+    """sa_mask_desc from a plain-dict mask spec; device inputs are appended to keep."""
+    d = L.MaskDesc()
+    d.num_blocks = int(spec["num_blocks"])
+    d.num_groups = int(spec["num_groups"])
+    d.causal = int(bool(spec["causal"]))
+    d.win_before = int(spec.get("win_before") or 0)
+    d.win_after = int(spec.get("win_after") or 0)
+    d.win_clamp = int(bool(spec.get("win_clamp")))
+    gl = [int(x) for x in (spec.get("global_blocks") or [])]
+    arr = (ctypes.c_int32 * max(1, len(gl)))(*gl)
+    keep.append(arr)
+    d.global_blocks = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    d.num_global = len(gl)
+    d.num_random = int(spec.get("num_random") or 0)
+    rb = spec.get("random_blocks")
+    if rb is not None:
+        t = torch.as_tensor(rb).to(device=device, dtype=torch.int32).contiguous()
+        keep.append(t)
+        d.random_blocks = t.data_ptr()
+    d.literal_mode = _LIT_MODES[spec.get("literal_mode") or "none"]
+    lf = spec.get("literal_flags")
+    if lf is not None:
+        t = torch.as_tensor(lf).to(device=device, dtype=torch.uint8).contiguous()
+        keep.append(t)
+        d.literal_flags = t.data_ptr()
+    d.literal_p = float(spec.get("literal_p") or 0.0)
+    d.seed = int(spec.get("seed") or 0) & ((1 << 64) - 1)
+    return d
+
+
+def sparse_attn_mask_capacity(spec):
+    keep = []
+    d = _mask_desc(spec, "cpu", keep)
+    cap = L.lib().sparse_attn_mask_capacity(ctypes.byref(d))
+    if cap < 0:
+        raise SparseAttnError(int(cap), "sparse_attn_mask_capacity")
+    return int(cap)
+
+
+def sparse_attn_check_mask_desc(spec):
+    keep = []
+    d = _mask_desc(spec, "cpu", keep)
+    return int(L.lib().sparse_attn_check_mask_desc(ctypes.byref(d)))
+
+
+def sparse_attn_build_mask(spec, device=None, schedule=True):
+    """Build the CSR block mask of ``spec`` on ``device`` (default: current GPU)."""
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    keep = []
+    d = _mask_desc(spec, device, keep)
+    cap = L.lib().sparse_attn_mask_capacity(ctypes.byref(d))
+    if cap < 0:
+        raise SparseAttnError(int(cap), "sparse_attn_build_mask")
+    R = d.num_groups * d.num_blocks
+    row_ptr = torch.empty(R + 1, dtype=torch.int32, device=device)
+    col_idx = torch.empty(max(1, cap), dtype=torch.int32, device=device)
+    sched = torch.empty((d.num_groups, d.num_blocks), dtype=torch.int32, device=device) if schedule else None
+    st = L.lib().sparse_attn_build_mask(ctypes.byref(d), _ptr(row_ptr), _ptr(col_idx), cap,
+                                        _ptr(sched), _stream(device))
+    _check(st, "sparse_attn_build_mask")
+    return BlockMask(row_ptr, col_idx, sched, d.num_groups, d.num_blocks, bool(d.causal))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return L.SA_BF16
+    if t.dtype == torch.float32:
+        return L.SA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_qkv(q, k, v):
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError("tensors must be [B, H, N, d] with d contiguous")
+        if t.device != q.device or t.dtype != q.dtype:
+            raise ValueError("q, k, v must share device and dtype")
+    B, H, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k, v must be [B, H_kv, N, d]")
+    return B, H, k.shape[1], N, d
+
+
+def _strides(*ts):
+    vals = []
+    for t in ts:
+        vals += [t.stride(0), t.stride(1), t.stride(2)]
+    return (ctypes.c_int64 * 12)(*vals)
+
+
+def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_stride=0,
+                    use_schedule=True, out=None, lse=None):
+    """Block-sparse attention; returns (o, lse).  ``mask`` is a BlockMask."""
+    B, H, Hkv, N, d = _check_qkv(q, k, v)
+    if N % mask.num_blocks:
+        raise ValueError("N must be a multiple of the number of mask blocks")
+    block = N // mask.num_blocks
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    sched = mask.sched if use_schedule else None
+    st = L.lib().sparse_attn_fwd(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, block,
+        _strides(q, k, v, o), _ptr(mask.row_ptr), _ptr(mask.col_idx), mask.col_idx.numel(),
+        _ptr(sched), mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal),
+        scale, _stream(q.device))
+    _check(st, "sparse_attn_fwd")
+    return o, lse_t
+
+
+def fibonacci_base(limit):
+    """1, 2, 3, 5, 8, ... below ``limit`` (the rung base of the offset pattern)."""
+    out, a, b = [], 1, 2
+    while a < limit:
+        out.append(a)
+        a, b = b, a + b
+    return out
+
+
+def offset_attn_make_table(W, alpha, base, N):
+    """Sorted distinct distances {0..W} U {floor(alpha f + 1/2)} below N (C helper)."""
+    K = len(base)
+    b = (ctypes.c_int64 * max(1, K))(*[int(x) for x in base])
+    cap = W + 1 + K
+    out = (ctypes.c_int32 * max(1, cap))()
+    cnt = ctypes.c_int32(0)
+    st = L.lib().offset_attn_make_table(int(W), float(alpha), b, K, int(N), out, cap, ctypes.byref(cnt))
+    _check(st, "offset_attn_make_table")
+    return [out[i] for i in range(cnt.value)]
+
+
+def offset_attn_fwd(q, k, v, offsets, scale=None, out=None, lse=None):
+    """Offset attention; ``offsets`` a host list of ascending distances."""
+    B, H, Hkv, N, d = _check_qkv(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    offs = [int(x) for x in offsets]
+    arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = L.lib().offset_attn_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                                 B, H, Hkv, N, d, _strides(q, k, v, o), arr, len(offs), scale,
+                                 _stream(q.device))
+    _check(st, "offset_attn_fwd")
+    return o, lse_t

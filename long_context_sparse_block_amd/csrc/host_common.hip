@@ -1,0 +1,86 @@
+// Status strings, the thread-local HIP error text and stride checks.
+#include <stddef.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sa_host.h"
+
+namespace {
+thread_local char g_last_error[256] = "";
+}
+
+namespace sa_host {
+
+sa_status record_hip_error(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return SA_ERR_HIP;
+}
+
+sa_status check_launch(const char* where) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return record_hip_error(e, where);
+  return SA_OK;
+}
+
+sa_status resolve_strides(const int64_t* strides, int32_t B, int32_t H, int32_t H_kv, int32_t N,
+                          int32_t d, int32_t align, Strides out[4]) {
+  const int32_t heads[4] = {H, H_kv, H_kv, H};
+  for (int t = 0; t < 4; ++t) {
+    if (strides == nullptr) {
+      out[t].s = d;
+      out[t].h = (int64_t)N * d;
+      out[t].b = (int64_t)heads[t] * N * d;
+    } else {
+      out[t].b = strides[3 * t + 0];
+      out[t].h = strides[3 * t + 1];
+      out[t].s = strides[3 * t + 2];
+    }
+    if (out[t].s < d || out[t].h < 0 || out[t].b < 0) return SA_ERR_INVALID;
+    if (out[t].s % align || out[t].h % align || out[t].b % align) return SA_ERR_INVALID;
+  }
+  (void)B;
+  return SA_OK;
+}
+
+}  // namespace sa_host
+
+extern "C" {
+
+const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "ok";
+    case SA_ERR_NULL: return "null pointer argument";
+    case SA_ERR_INVALID: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_CAPACITY: return "output buffer too small";
+    case SA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sa_last_hip_error(void) { return g_last_error; }
+
+int32_t sa_version(void) { return 1; }
+
+int32_t sa_mask_desc_layout(int64_t* out, int32_t n) {
+  const int64_t v[15] = {(int64_t)sizeof(sa_mask_desc),
+                         (int64_t)offsetof(sa_mask_desc, num_blocks),
+                         (int64_t)offsetof(sa_mask_desc, num_groups),
+                         (int64_t)offsetof(sa_mask_desc, causal),
+                         (int64_t)offsetof(sa_mask_desc, win_before),
+                         (int64_t)offsetof(sa_mask_desc, win_after),
+                         (int64_t)offsetof(sa_mask_desc, win_clamp),
+                         (int64_t)offsetof(sa_mask_desc, global_blocks),
+                         (int64_t)offsetof(sa_mask_desc, num_global),
+                         (int64_t)offsetof(sa_mask_desc, num_random),
+                         (int64_t)offsetof(sa_mask_desc, random_blocks),
+                         (int64_t)offsetof(sa_mask_desc, literal_mode),
+                         (int64_t)offsetof(sa_mask_desc, literal_flags),
+                         (int64_t)offsetof(sa_mask_desc, literal_p),
+                         (int64_t)offsetof(sa_mask_desc, seed)};
+  if (out == nullptr) return 15;
+  for (int32_t i = 0; i < n && i < 15; ++i) out[i] = v[i];
+  return 15;
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, matches the binding's struct layout, and rejects bad arguments on the
+host before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_block_amd import _lib as L
+from long_context_sparse_block_amd import api
+from oracle import offsets as oo
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparse_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "return")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("library not built")
+    return L.lib()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared_functions()
+    assert {"sparse_attn_build_mask", "sparse_attn_fwd", "offset_attn_fwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, n
+
+
+def test_mask_desc_layout_matches_binding(lib):
+    out = (ctypes.c_int64 * 15)()
+    assert lib.sa_mask_desc_layout(out, 15) == 15
+    fields = [f[0] for f in L.MaskDesc._fields_]
+    assert out[0] == ctypes.sizeof(L.MaskDesc)
+    for n, name in enumerate(fields):
+        assert out[n + 1] == getattr(L.MaskDesc, name).offset, name
+
+
+def test_status_strings(lib):
+    for st in (L.SA_OK, L.SA_ERR_NULL, L.SA_ERR_INVALID, L.SA_ERR_UNSUPPORTED, L.SA_ERR_CAPACITY, L.SA_ERR_HIP):
+        assert L.status_string(st)
+    assert lib.sa_version() >= 1
+
+
+def _spec(**kw):
+    s = dict(num_blocks=8, num_groups=1, causal=True, win_before=1, win_after=0, win_clamp=False,
+             global_blocks=[0], num_random=1, literal_mode="none", literal_p=0.0, seed=1)
+    s.update(kw)
+    return s
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_blocks=0), L.SA_ERR_INVALID),
+    (dict(num_blocks=L.SA_MAX_BLOCKS + 1), L.SA_ERR_INVALID),
+    (dict(num_groups=0), L.SA_ERR_INVALID),
+    (dict(win_before=-1), L.SA_ERR_INVALID),
+    (dict(win_after=1), L.SA_ERR_INVALID),              # causal window may not look ahead
+    (dict(global_blocks=[3, 2]), L.SA_ERR_INVALID),     # not ascending
+    (dict(global_blocks=[0, 0]), L.SA_ERR_INVALID),     # repeated
+    (dict(global_blocks=[8]), L.SA_ERR_INVALID),        # out of range
+    (dict(num_random=L.SA_MAX_RANDOM + 1), L.SA_ERR_INVALID),
+    (dict(literal_mode="pair", literal_p=1.5), L.SA_ERR_INVALID),
+    (dict(causal=False, num_blocks=16384, num_groups=16), L.SA_ERR_UNSUPPORTED),
+])
+def test_mask_desc_errors(lib, over, status):
+    assert api.sparse_attn_check_mask_desc(_spec(**over)) == status
+
+
+def test_mask_capacity(lib):
+    assert api.sparse_attn_mask_capacity(_spec()) == 8 * 9 // 2
+    assert api.sparse_attn_mask_capacity(_spec(causal=False, num_groups=3)) == 3 * 64
+    assert api.sparse_attn_check_mask_desc(_spec()) == L.SA_OK
+
+
+def test_build_mask_host_errors(lib):
+    d = L.MaskDesc()
+    keep = []
+    d = api._mask_desc(_spec(), "cpu", keep)
+    fake = ctypes.c_void_p(1 << 20)
+    # NULL outputs
+    assert lib.sparse_attn_build_mask(ctypes.byref(d), None, fake, 100, None, None) == L.SA_ERR_NULL
+    # capacity below the bound
+    assert lib.sparse_attn_build_mask(ctypes.byref(d), fake, fake, 35, None, None) == L.SA_ERR_CAPACITY
+    assert lib.sparse_attn_build_mask(None, fake, fake, 100, None, None) == L.SA_ERR_NULL
+
+
+def _fwd(lib, **kw):
+    fake = ctypes.c_void_p(1 << 20)
+    a = dict(dtype=L.SA_BF16, q=fake, k=fake, v=fake, o=fake, lse=fake, B=1, H=2, H_kv=2, N=512,
+             d=64, block=64, strides=None, row_ptr=fake, col_idx=fake, cap=100, sched=None, G=1,
+             mbs=0, mhs=0, causal=1, scale=0.125)
+    a.update(kw)
+    return lib.sparse_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                               a["H_kv"], a["N"], a["d"], a["block"], a["strides"], a["row_ptr"],
+                               a["col_idx"], a["cap"], a["sched"], a["G"], a["mbs"], a["mhs"],
+                               a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), L.SA_ERR_NULL),
+    (dict(row_ptr=None), L.SA_ERR_NULL),
+    (dict(dtype=7), L.SA_ERR_INVALID),
+    (dict(N=500), L.SA_ERR_INVALID),                 # N % block != 0
+    (dict(H=3, H_kv=2), L.SA_ERR_INVALID),
+    (dict(d=96), L.SA_ERR_UNSUPPORTED),
+    (dict(block=32), L.SA_ERR_UNSUPPORTED),
+    (dict(G=1, mhs=1), L.SA_ERR_INVALID),            # head group index out of range
+    (dict(causal=2), L.SA_ERR_INVALID),
+    (dict(scale=float("nan")), L.SA_ERR_INVALID),
+    (dict(cap=-1), L.SA_ERR_INVALID),
+    (dict(q=ctypes.c_void_p((1 << 20) + 2)), L.SA_ERR_INVALID),  # misaligned
+    (dict(strides=(ctypes.c_int64 * 12)(*([8192 * 64, 8192 * 64, 60] * 4))), L.SA_ERR_INVALID),
+    (dict(strides=(ctypes.c_int64 * 12)(*([8192 * 64, 8192 * 64, 68] * 4))), L.SA_ERR_INVALID),
+])
+def test_fwd_host_errors(lib, over, status):
+    assert _fwd(lib, **over) == status
+
+
+def _off(lib, offsets, **kw):
+    fake = ctypes.c_void_p(1 << 20)
+    a = dict(dtype=L.SA_BF16, B=1, H=1, H_kv=1, N=64, d=64)
+    a.update(kw)
+    arr = (ctypes.c_int32 * max(1, len(offsets)))(*offsets)
+    return lib.offset_attn_fwd(a["dtype"], fake, fake, fake, fake, fake, a["B"], a["H"], a["H_kv"],
+                               a["N"], a["d"], None, arr, len(offsets), 0.125, None)
+
+
+@pytest.mark.parametrize("offsets,over,status", [
+    ([], {}, L.SA_ERR_INVALID),
+    ([0, 2, 1], {}, L.SA_ERR_INVALID),
+    ([0, 1, 1], {}, L.SA_ERR_INVALID),
+    ([0, 64], {}, L.SA_ERR_INVALID),
+    ([-1, 0], {}, L.SA_ERR_INVALID),
+    (list(range(L.SA_MAX_OFFSETS + 1)), dict(N=4096), L.SA_ERR_INVALID),
+    ([0, 1], dict(d=32), L.SA_ERR_UNSUPPORTED),
+    ([0, 1], dict(H=2, H_kv=3), L.SA_ERR_INVALID),
+])
+def test_offset_host_errors(lib, offsets, over, status):
+    assert _off(lib, offsets, **over) == status
+
+
+def test_offset_table_matches_oracle(lib):
+    for N in (64, 1000, 2048, 8192):
+        base = oo.fibonacci_base(N)
+        assert api.fibonacci_base(N) == base
+        for l in range(16):
+            a = 1.0 + l / 15.0
+            assert api.offset_attn_make_table(8, a, base, N) == oo.offset_table(8, a, base, N)
+    assert api.offset_attn_make_table(0, 0.5, [1, 3], 10) == [0, 1, 2]
+    assert api.offset_attn_make_table(3, 1.0, [100], 50) == [0, 1, 2, 3]
+
+
+def test_offset_table_capacity_error(lib):
+    out = (ctypes.c_int32 * 2)()
+    cnt = ctypes.c_int32()
+    b = (ctypes.c_int64 * 1)(5)
+    assert lib.offset_attn_make_table(3, 1.0, b, 1, 100, out, 2, ctypes.byref(cnt)) == L.SA_ERR_CAPACITY

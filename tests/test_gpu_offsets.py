@@ -1,0 +1,102 @@
+"""GPU offset attention vs the oracle: all 16 staggered calls at reduced batch,
+sampled rows at full size, special tables and ragged lengths."""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_block_amd import api
+from long_context_sparse_block_amd import workloads as wl
+from oracle import offsets as oo
+from tests.gpu_util import announce, compare, f64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+W = wl.OFFSET_WORKLOAD
+
+
+def _table(alpha, N):
+    return oo.offset_table(W["W"], alpha, oo.fibonacci_base(N), N)
+
+
+@pytest.mark.parametrize("N", W["lengths"])
+def test_all_alphas_reduced_batch(N):
+    require_gpu()
+    B, H = 1, 2
+    for l, alpha in enumerate(W["alphas"]):
+        offs = _table(alpha, N)
+        q, k, v = wl.make_qkv(B, H, N, W["d"], torch.bfloat16, W["qkv_seed_base"][N] + l)
+        announce(f"[offset] N={N} alpha={alpha:.4f} |D|={len(offs)}")
+        o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 1 / math.sqrt(W["d"]))
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"N={N} l={l}")
+
+
+@pytest.mark.parametrize("N", W["lengths"])
+def test_full_size_sampled(N):
+    require_gpu()
+    B, H, d = W["B"], W["H"], W["d"]
+    R = random.Random(N)
+    samples = sorted({(0, 0, 0), (B - 1, H - 1, N - 1)} |
+                     {(R.randrange(B), R.randrange(H), R.randrange(N)) for _ in range(94)})
+    for l in (0, 7, 15):
+        alpha = W["alphas"][l]
+        offs = _table(alpha, N)
+        q, k, v = wl.make_qkv(B, H, N, d, torch.bfloat16, W["qkv_seed_base"][N] + l)
+        announce(f"[offset] full {B}x{H}x{N}x{d} l={l}")
+        o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oo.offset_attention_rows(f64(q), f64(k), f64(v), offs, 1 / math.sqrt(d), samples)
+        og = torch.stack([o[b, h, t] for b, h, t in samples])
+        lg = torch.stack([lse[b, h, t] for b, h, t in samples])
+        compare(og, lg, o_ref, l_ref, torch.bfloat16, f"full N={N} l={l}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_lengths_and_dtypes(dtype, d):
+    require_gpu()
+    for N in (1, 63, 257, 1000):
+        offs = oo.offset_table(5, 1.3, oo.fibonacci_base(N), N)
+        q, k, v = wl.make_qkv(2, 2, N, d, dtype, 500 + N)
+        announce(f"[offset] ragged N={N} d={d} {dtype}")
+        o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs, 0.2)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 0.2)
+        compare(o, lse, o_ref, l_ref, dtype, f"ragged N={N}")
+
+
+def test_zero_table_is_identity_fp32():
+    require_gpu()
+    q, k, v = [t.cuda() for t in wl.make_qkv(1, 2, 300, 64, torch.float32, 8)]
+    announce("[offset] table {0}")
+    o, lse = api.offset_attn_fwd(q, k, v, [0], 0.3)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
+
+
+def test_full_table_is_dense_causal():
+    require_gpu()
+    N = 128
+    q, k, v = wl.make_qkv(1, 2, N, 64, torch.float32, 9)
+    announce("[offset] table {0..N-1}")
+    o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), list(range(N)), 0.125)
+    torch.cuda.synchronize()
+    ref = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double(),
+                                                           is_causal=True, scale=0.125)
+    assert (o.cpu().double() - ref).abs().max() < 1e-5
+
+
+def test_gqa_offsets():
+    require_gpu()
+    q, k, v = wl.make_qkv(2, 4, 512, 64, torch.bfloat16, 10, H_kv=1)
+    offs = _table(1.5, 512)
+    announce("[offset] gqa")
+    o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 0.125)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, "gqa")
