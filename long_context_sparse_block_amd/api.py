@@ -196,3 +196,72 @@ def offset_attn_fwd(q, k, v, offsets, scale=None, out=None, lse=None):
                                  _stream(q.device))
     _check(st, "offset_attn_fwd")
     return o, lse_t
+
+
+class BlockSparsePlan:
+    """Preallocated buffers and pre-marshalled arguments for repeated
+    (mask build, block-sparse forward) steps on fixed shapes.
+
+    ``build_mask()`` and ``forward()`` each make one C call and allocate
+    nothing; outputs land in ``self.mask``, ``self.o`` and ``self.lse``.
+    """
+
+    def __init__(self, spec, q, k, v, scale=None, use_schedule=True):
+        B, H, Hkv, N, d = _check_qkv(q, k, v)
+        self.device = q.device
+        self._keep = []
+        self._desc = _mask_desc(spec, q.device, self._keep)
+        cap = L.lib().sparse_attn_mask_capacity(ctypes.byref(self._desc))
+        if cap < 0:
+            raise SparseAttnError(int(cap), "BlockSparsePlan")
+        G, nb = self._desc.num_groups, self._desc.num_blocks
+        if N % nb:
+            raise ValueError("N must be a multiple of the number of mask blocks")
+        self.mask = BlockMask(torch.empty(G * nb + 1, dtype=torch.int32, device=q.device),
+                              torch.empty(max(1, cap), dtype=torch.int32, device=q.device),
+                              torch.empty((G, nb), dtype=torch.int32, device=q.device) if use_schedule else None,
+                              G, nb, bool(self._desc.causal))
+        self.q, self.k, self.v = q, k, v
+        self.o = torch.empty_like(q, memory_format=torch.contiguous_format)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        self.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        self.mbs = int(spec.get("mask_batch_stride", 0))
+        self.mhs = int(spec.get("mask_head_stride", 0))
+        self._fwd_args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(self.o), _ptr(self.lse), B, H,
+                          Hkv, N, d, N // nb, _strides(q, k, v, self.o), _ptr(self.mask.row_ptr),
+                          _ptr(self.mask.col_idx), self.mask.col_idx.numel(), _ptr(self.mask.sched),
+                          G, self.mbs, self.mhs, int(self._desc.causal), self.scale)
+        self._mask_args = (ctypes.byref(self._desc), _ptr(self.mask.row_ptr), _ptr(self.mask.col_idx),
+                           self.mask.col_idx.numel(), _ptr(self.mask.sched))
+        self._lib = L.lib()
+
+    def build_mask(self):
+        _check(self._lib.sparse_attn_build_mask(*self._mask_args, _stream(self.device)), "sparse_attn_build_mask")
+
+    def forward(self):
+        _check(self._lib.sparse_attn_fwd(*self._fwd_args, _stream(self.device)), "sparse_attn_fwd")
+
+    def __call__(self):
+        self.build_mask()
+        self.forward()
+        return self.o, self.lse
+
+
+class OffsetPlan:
+    """Pre-marshalled offset_attn_fwd call on fixed tensors (allocates nothing per call)."""
+
+    def __init__(self, q, k, v, offsets, scale=None):
+        B, H, Hkv, N, d = _check_qkv(q, k, v)
+        self.device = q.device
+        offs = [int(x) for x in offsets]
+        self._arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
+        self.o = torch.empty_like(q, memory_format=torch.contiguous_format)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        self._args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(self.o), _ptr(self.lse), B, H, Hkv,
+                      N, d, _strides(q, k, v, self.o), self._arr, len(offs), scale)
+        self._lib = L.lib()
+
+    def __call__(self):
+        _check(self._lib.offset_attn_fwd(*self._args, _stream(self.device)), "offset_attn_fwd")
+        return self.o, self.lse
