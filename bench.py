@@ -187,6 +187,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernel", choices=sorted(wl.BLOCK_WORKLOADS) + ["offsets-2048", "offsets-8192"],
+                    help="run only the given workload's kernels (for counter collection), then exit")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (traffic-counter calibration), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -194,6 +198,24 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": args.steps}))
+        return
+    if args.profile_kernel:
+        if args.profile_kernel.startswith("offsets"):
+            r = offset_workload(int(args.profile_kernel.split("-")[1]), reps=args.steps, warmup=0)
+            print(json.dumps({"workload": args.profile_kernel, "call_ms": r["call_ms"], "gbs": r["gbs"]}))
+        else:
+            r = block_workload(args.profile_kernel, steps=1, warmup=0, kernel_iters=args.steps)
+            print(json.dumps({"workload": args.profile_kernel, "fwd_ms": r["fwd_ms"],
+                              "tflops": r["flops"] / (r["fwd_ms"] * 1e-3) / 1e12}))
+        return
 
     head = block_workload(HEADLINE, args.steps, args.warmup, kernel_iters=max(50, args.steps))
     w = head["w"]

@@ -34,6 +34,8 @@ def compile_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
             # packed fp32 VALU ops stay disabled on this target
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in plain VGPRs: no copies between register files
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
             "-I", INCLUDE, "-I", CSRC]
 

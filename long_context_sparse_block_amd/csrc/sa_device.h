@@ -52,4 +52,36 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 
 __device__ __forceinline__ int wave_lane() { return __lane_id(); }
 
+// Target builtins are wrapped in plain (non-template) device functions: a
+// kernel template that names them directly is not instantiated by the host
+// pass, and its launch stub would be missing.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (lds_base must be the same for the whole wave).  Issued as inline asm so the
+// compiler does not track it: it would otherwise wait for every outstanding
+// DMA before any later LDS read, which serialises a multi-stage ring.  The
+// caller orders the DMA with explicit "s_waitcnt vmcnt" + barrier.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+  uint32_t saved;  // M0 is restored so code around the asm may keep using it
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// Transpose read of 4 x 16-bit values: within each group of 16 lanes, lane i
+// receives element (i % 4) of the 8-byte words read by lanes i/4, i/4 + 4,
+// i/4 + 8 and i/4 + 12 of the group (in that order).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
+  typedef __attribute__((ext_vector_type(4))) short s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 }  // namespace sa
