@@ -3,18 +3,26 @@
 // every distance delta of a table shared by all queries (a dense window
 // {0..W} plus rounded scaled Fibonacci rungs), skipping t - delta < 0.
 //
-// The work per (query, key) is a single dot product and a single V update, so
-// the kernel is bound by memory traffic, not by matrix throughput: one thread
-// owns one query, keeps q and the fp32 accumulator in registers, and walks the
-// table in chunks of 8 distances (8 dot products, one softmax rescale, 8 V
-// updates).  Consecutive threads own consecutive queries, so for a fixed
-// distance a wave reads one contiguous span of K / V rows.  Every K / V row is
-// referenced by |table| different queries; those re-reads are served by L2:
-// the workgroups of one head are mapped to one XCD (blockIdx % 8 selects the
-// XCD) and the heads of an XCD are walked one after another.
+// Every (query, key) pair is a single dot product and a single V update, so
+// the work is bound by moving K / V rows, not by matrix throughput.  bf16 path:
+//   * a workgroup owns 64 consecutive queries of one head; four lanes share a
+//     query, each holding a quarter of the head dimension, so the rows read for
+//     a fixed distance form contiguous, fully used 64-byte segments and the
+//     dot product needs only two quad (DPP) reductions;
+//   * the near distances (<= 64) all read inside the span [t0 - R, t0 + 64)
+//     (R = the largest near distance), which is staged once in LDS; the far
+//     rungs are read straight from global memory / L2;
+//   * distances are taken 8 at a time: 8 scores, one online-softmax rescale,
+//     then V is accumulated two keys at a time with bf16 dot2 (the two keys'
+//     values for one column are paired with a byte permute), one instruction
+//     per two multiply-adds;
+//   * workgroups of one head run on one XCD (blockIdx % 8 selects the XCD), so
+//     every re-read of a K / V row by another query tile is served by its L2.
+// fp32 path: one thread per query, plain fp32 arithmetic, for exact checks.
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "sa_device.h"
@@ -24,6 +32,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;
+constexpr int kNearMax = 64;   // distances up to this are served from the staged span
+
+// Raise the dynamic-LDS limit of a kernel once (needed above 64 KiB).
+inline sa_status allow_lds(const void* kern, int bytes) {
+  if (bytes <= 65536) return SA_OK;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return e == hipSuccess ? SA_OK : sa_host::record_hip_error(e, "hipFuncSetAttribute");
+}
+
+
 
 struct OffArgs {
   const void* q;
@@ -33,6 +51,8 @@ struct OffArgs {
   float* lse;
   int64_t qs[3], ks[3], vs[3], os[3];
   int32_t B, H, H_kv, N, noff;
+  int32_t nnear;  // offsets[0 .. nnear) are <= kNearMax and are read from the staged span
+  int32_t span_r; // largest near offset (rows staged before the tile)
   float scale_log2;
   int32_t offs[SA_MAX_OFFSETS];
 };
@@ -70,14 +90,10 @@ __device__ __forceinline__ void load_row(const typename Elem<BF16>::T* p, float*
   }
 }
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void offset_fwd_kernel(OffArgs a) {
-  typedef typename Elem<BF16>::T T;
-  const int tiles = (a.N + kThreads - 1) / kThreads;
-  const int BH = a.B * a.H;
-  const int w = blockIdx.x;
-  int bh, tile;
-  if ((BH & 7) == 0) {  // keep all tiles of a head on one XCD
+// (head, tile) of a workgroup; with B*H a multiple of 8 all tiles of a head go
+// to one XCD (workgroup ids are dealt to the 8 XCDs round robin).
+__device__ __forceinline__ void tile_of(int w, int BH, int tiles, int& bh, int& tile) {
+  if ((BH & 7) == 0) {
     const int xcd = w & 7, slot = w >> 3;
     bh = xcd + 8 * (slot / tiles);
     tile = slot % tiles;
@@ -85,6 +101,189 @@ __global__ __launch_bounds__(kThreads) void offset_fwd_kernel(OffArgs a) {
     bh = w / tiles;
     tile = w % tiles;
   }
+}
+
+// 16-byte chunk slot inside a staged row (XOR swizzle against bank conflicts
+// between the 16 rows one wave-instruction touches).
+__device__ __forceinline__ int swz_row(int c, int row) { return c ^ (row & 7); }
+
+// (v_a, v_b) bf16 pairs -> (lo halves), (hi halves)
+__device__ __forceinline__ uint32_t pair_lo(uint32_t va, uint32_t vb) { return __builtin_amdgcn_perm(vb, va, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t va, uint32_t vb) { return __builtin_amdgcn_perm(vb, va, 0x07060302u); }
+
+// Sum over the 4 lanes of a quad (DPP quad permutes, no LDS traffic).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
+
+template <int D>
+struct OffCfg {
+  static constexpr int LPQ = 4;                 // lanes per query
+  static constexpr int TQ = 64;                 // queries per workgroup
+  static constexpr int NT = TQ * LPQ;           // threads
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int CPL = CPR / LPQ;         // chunks per lane: c = j + 4 m
+  static constexpr int ROWB = D * 2;
+  static constexpr int SPAN = TQ + kNearMax;    // staged rows
+  static constexpr int LDSB = 2 * SPAN * ROWB;  // K and V
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void offset_bf16_kernel(OffArgs a) {
+  using C = OffCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* ks = smem;
+  uint8_t* vs = smem + C::SPAN * C::ROWB;
+
+  const int tid = threadIdx.x;
+  const int ql = tid / C::LPQ, j = tid % C::LPQ;
+  const int tiles = (a.N + C::TQ - 1) / C::TQ;
+  int bh, tile;
+  tile_of(blockIdx.x, a.B * a.H, tiles, bh, tile);
+  const int b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
+  const int t0 = tile * C::TQ;
+  const int t = t0 + ql;
+  const bool live = t < a.N;
+  const int tq = live ? t : a.N - 1;
+
+  const uint16_t* Q = (const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1];
+  const char* Kb = (const char*)((const uint16_t*)a.k + b * a.ks[0] + kvh * a.ks[1]);
+  const char* Vb = (const char*)((const uint16_t*)a.v + b * a.vs[0] + kvh * a.vs[1]);
+  const uint32_t krow = (uint32_t)a.ks[2] * 2u, vrow = (uint32_t)a.vs[2] * 2u;  // bytes per row
+
+  // stage rows [t0 - R, t0 + TQ) of K and V (rows outside [0, N) are skipped;
+  // no query reads them)
+  const int R = a.span_r;
+  const int rows = C::TQ + R;
+  for (int x = tid; x < rows * C::CPR; x += C::NT) {
+    const int lr = x / C::CPR, c = x % C::CPR;
+    const int r = t0 - R + lr;
+    if (r < 0 || r >= a.N) continue;
+    const int off = lr * C::ROWB + swz_row(c, lr) * 16;
+    *(sa::u32x4*)(ks + off) = *(const sa::u32x4*)(Kb + (uint32_t)r * krow + 16u * c);
+    *(sa::u32x4*)(vs + off) = *(const sa::u32x4*)(Vb + (uint32_t)r * vrow + 16u * c);
+  }
+
+  // this lane's quarter of q: chunks c = j + 4 m
+  sa::u32x4 qv[C::CPL];
+#pragma unroll
+  for (int m = 0; m < C::CPL; ++m) qv[m] = *(const sa::u32x4*)(Q + (int64_t)tq * a.qs[2] + 8 * (j + 4 * m));
+  float acc[C::CPL][8];
+#pragma unroll
+  for (int m = 0; m < C::CPL; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+  __syncthreads();
+
+  // One chunk of 8 distances [n0, n0 + 8) (entries past n1 repeat the range's
+  // last distance and get weight 0): scores, one rescale, V update.  FAR rows
+  // come from global memory, near ones from the staged span; MASKED: some
+  // query of the tile precedes a distance of the chunk.
+  auto chunk = [&](int n0, int n1, auto far_t, auto masked_t) {
+    constexpr bool FAR = decltype(far_t)::value;
+    constexpr bool MASKED = decltype(masked_t)::value;
+    int src[kChunk];
+    bool ok[kChunk];
+#pragma unroll
+    for (int cc = 0; cc < kChunk; ++cc) {
+      const int delta = a.offs[min(n0 + cc, n1 - 1)];
+      int s0 = tq - delta;
+      ok[cc] = !MASKED || s0 >= 0;
+      if (MASKED) s0 = max(s0, 0);
+      src[cc] = FAR ? s0 : s0 - (t0 - R);  // global row, or row of the span
+    }
+    auto ld = [&](const char* g, const uint8_t* l, uint32_t grow, int cc, int m) -> sa::u32x4 {
+      const int c = j + 4 * m;
+      if (FAR) return *(const sa::u32x4*)(g + (uint32_t)src[cc] * grow + 16u * c);
+      return *(const sa::u32x4*)(l + src[cc] * C::ROWB + swz_row(c, src[cc]) * 16);
+    };
+    float y[kChunk];
+#pragma unroll
+    for (int cc = 0; cc < kChunk; ++cc) {
+      float dot = 0.f;
+#pragma unroll
+      for (int m = 0; m < C::CPL; ++m) {
+        const sa::u32x4 kv = ld(Kb, ks, krow, cc, m);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dot = sa::dot2_bf16(qv[m][w], kv[w], dot);
+      }
+      dot = quad_sum(dot) * c2;
+      y[cc] = (n0 + cc < n1 && ok[cc]) ? dot : -INFINITY;
+    }
+    float mx = y[0];
+#pragma unroll
+    for (int cc = 1; cc < kChunk; ++cc) mx = fmaxf(mx, y[cc]);
+    if (mx > m_run) {  // per query (the quad agrees); rescale the running state
+      const float alpha = sa::fast_exp2(m_run - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < C::CPL; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[m][e] *= alpha;
+      m_run = mx;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int cc = 0; cc < kChunk; cc += 2) {
+      const uint32_t pp = sa::pack_bf16x2(sa::fast_exp2(y[cc] - m_use), sa::fast_exp2(y[cc + 1] - m_use));
+      l_run = sa::dot2_bf16(pp, 0x3f803f80u, l_run);
+#pragma unroll
+      for (int m = 0; m < C::CPL; ++m) {
+        sa::u32x4 va = ld(Vb, vs, vrow, cc, m);
+        sa::u32x4 vb = ld(Vb, vs, vrow, cc + 1, m);
+        if (MASKED) {  // keys before the sequence start: zero weight and zero value
+          if (!ok[cc]) va = sa::u32x4{0u, 0u, 0u, 0u};
+          if (!ok[cc + 1]) vb = sa::u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[m][2 * w] = sa::dot2_bf16(pp, pair_lo(va[w], vb[w]), acc[m][2 * w]);
+          acc[m][2 * w + 1] = sa::dot2_bf16(pp, pair_hi(va[w], vb[w]), acc[m][2 * w + 1]);
+        }
+      }
+    }
+  };
+
+  // near distances from LDS, then far ones from global memory; a chunk needs
+  // masking only if the tile's first query precedes its largest distance
+  for (int n0 = 0; n0 < a.nnear; n0 += kChunk) {
+    const int n1 = min(n0 + kChunk, a.nnear);
+    if (t0 >= a.offs[n1 - 1])
+      chunk(n0, n1, std::false_type{}, std::false_type{});
+    else
+      chunk(n0, n1, std::false_type{}, std::true_type{});
+  }
+  for (int n0 = a.nnear; n0 < a.noff; n0 += kChunk) {
+    const int n1 = min(n0 + kChunk, a.noff);
+    if (t0 >= a.offs[n1 - 1])
+      chunk(n0, n1, std::true_type{}, std::false_type{});
+    else
+      chunk(n0, n1, std::true_type{}, std::true_type{});
+  }
+
+  if (!live) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  uint16_t* O = (uint16_t*)a.o + b * a.os[0] + h * a.os[1] + (int64_t)t * a.os[2];
+#pragma unroll
+  for (int m = 0; m < C::CPL; ++m) {
+    sa::u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = sa::pack_bf16x2(acc[m][2 * e] * inv, acc[m][2 * e + 1] * inv);
+    *(sa::u32x4*)(O + 8 * (j + 4 * m)) = w;
+  }
+  if (j == 0) a.lse[((int64_t)b * a.H + h) * a.N + t] = l_run > 0.f ? (m_run + log2f(l_run)) * sa::kLn2 : -INFINITY;
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void offset_fwd_kernel(OffArgs a) {
+  typedef typename Elem<BF16>::T T;
+  const int tiles = (a.N + kThreads - 1) / kThreads;
+  int bh, tile;
+  tile_of(blockIdx.x, a.B * a.H, tiles, bh, tile);
   const int b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
   const int t = tile * kThreads + threadIdx.x;
   if (t >= a.N) return;
@@ -218,13 +417,25 @@ extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k
   a.B = B, a.H = H, a.H_kv = H_kv, a.N = N, a.noff = num_offsets;
   a.scale_log2 = scale * sa::kLog2e;
   for (int n = 0; n < num_offsets; ++n) a.offs[n] = offsets[n];
-  const dim3 grid((unsigned)((int64_t)B * H * tiles));
+  a.nnear = 0;
+  a.span_r = 0;
+  while (a.nnear < num_offsets && offsets[a.nnear] <= kNearMax) a.span_r = offsets[a.nnear++];
   if (dtype == SA_BF16) {
-    if (d == 64)
-      hipLaunchKernelGGL((offset_fwd_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((offset_fwd_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+    if (d == 64) {
+      using Cf = OffCfg<64>;
+      static const sa_status lds_ok = allow_lds((const void*)&offset_bf16_kernel<64>, Cf::LDSB);
+      if (lds_ok != SA_OK) return lds_ok;
+      const dim3 grid((unsigned)((int64_t)B * H * ((N + Cf::TQ - 1) / Cf::TQ)));
+      hipLaunchKernelGGL((offset_bf16_kernel<64>), grid, dim3(Cf::NT), Cf::LDSB, stream, a);
+    } else {
+      using Cf = OffCfg<128>;
+      static const sa_status lds_ok = allow_lds((const void*)&offset_bf16_kernel<128>, Cf::LDSB);
+      if (lds_ok != SA_OK) return lds_ok;
+      const dim3 grid((unsigned)((int64_t)B * H * ((N + Cf::TQ - 1) / Cf::TQ)));
+      hipLaunchKernelGGL((offset_bf16_kernel<128>), grid, dim3(Cf::NT), Cf::LDSB, stream, a);
+    }
   } else {
+    const dim3 grid((unsigned)((int64_t)B * H * tiles));
     if (d == 64)
       hipLaunchKernelGGL((offset_fwd_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
     else
