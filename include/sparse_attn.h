@@ -165,7 +165,9 @@ sa_status sparse_attn_build_mask(const sa_mask_desc* desc, int32_t* row_ptr, int
  *   sched      DEVICE int32 [num_groups][N_b] launch order or NULL.
  *   num_groups G; (B-1)*mask_batch_stride + (H-1)*mask_head_stride < G,
  *              strides >= 0.
- *   scale      logit scale, e.g. 1/sqrt(d)
+ *   scale      logit scale, e.g. 1/sqrt(d) (any finite value, 0 and < 0 included)
+ *   SA_ERR_UNSUPPORTED for bf16 when a K or V sequence stride is >= 2^24
+ *              elements.
  */
 sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o,
                           float* lse, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,

@@ -10,24 +10,28 @@
 //
 // bf16 path (MFMA, gfx950):
 //   * one workgroup per (batch, head, query block); one wave per 32 queries;
-//   * key blocks are walked in 64-key sub-tiles; K (row-major) and V (stored
-//     transposed) of the next sub-tile are fetched into registers while the
-//     current one is consumed from LDS (two LDS stages, one barrier per step);
+//     optionally NP groups of waves split the row's key tiles and merge;
+//   * key blocks are walked in 64-key tiles copied global -> LDS by direct
+//     (DMA) loads into rings of K and V slots; for d = 64 the K ring runs one
+//     tile ahead so that S(n+1) is computed on the matrix cores while the
+//     softmax of tile n runs on the VALU;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so every lane owns one query
 //     column: the row max / sum of the online softmax are in-lane except for a
-//     single exchange with lane ^ 32;
+//     single exchange with lane ^ 32 (v_permlane32_swap);
 //   * O^T += V^T P^T on the same MFMA: the fp32 accumulator of S^T already holds
 //     exactly the keys each lane must supply as the P operand, so P goes from
 //     the accumulator to the operand registers with one bf16 pack and no LDS
-//     round trip.  V is written to LDS transposed, with key bits 2 and 3 swapped
-//     so that each lane reads its 8 keys as one 16-byte word;
-//   * 16-byte LDS chunks are XOR-swizzled so the MFMA operand reads and the
-//     staging writes are free of bank conflicts;
+//     round trip.  The V^T operand comes from row-major V in LDS through
+//     transpose reads (ds_read_b64_tr_b16);
+//   * 16-byte LDS chunks are XOR-swizzled so the MFMA operand reads are free of
+//     bank conflicts;
 //   * launch order follows `sched` (longest rows first); blockIdx % (B*H) picks
 //     the head, so with B*H a multiple of 8 every query block of one head runs
 //     on the same XCD and shares its L2.
 // fp32 path: a plain VALU kernel, one thread per query, for exact checks.
 #include <math.h>
+
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_host.h"
@@ -49,13 +53,14 @@ struct BsaArgs {
   int64_t mbs, mhs;
   int32_t causal;
   float scale;       // logit scale
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // |scale| * log2(e) (bf16 path), never 0
+  uint32_t qsign;    // bf16 pair sign mask folded into Q when scale < 0
 };
 
 // Work item of a workgroup: head (b, h), query block i, CSR entry range.
 struct Item {
   int32_t b, h, kvh, i;
-  int64_t e_beg, e_end;
+  int32_t e_beg, e_end;
   bool ok;
 };
 
@@ -68,14 +73,16 @@ __device__ __forceinline__ Item work_item(const BsaArgs& a) {
   it.h = bh - it.b * a.H;
   it.kvh = it.h / (a.H / a.H_kv);
   const int64_t g = (int64_t)it.b * a.mbs + (int64_t)it.h * a.mhs;
-  it.i = a.sched ? a.sched[g * a.nb + pos] : pos;
+  it.i = sa::uniform(a.sched ? a.sched[g * a.nb + pos] : pos);
   it.ok = it.i >= 0 && it.i < a.nb;
   const int64_t r = g * a.nb + (it.ok ? it.i : 0);
   int64_t e0 = a.row_ptr[r], e1 = a.row_ptr[r + 1];
   e0 = max((int64_t)0, min(e0, a.col_capacity));
   e1 = max(e0, min(e1, a.col_capacity));
-  it.e_beg = e0;
-  it.e_end = e1;
+  // row_ptr entries are int32, so the clamped range fits in 32 bits; the
+  // values are the same in every lane (made visible to the compiler)
+  it.e_beg = sa::uniform((int32_t)e0);
+  it.e_end = sa::uniform((int32_t)e1);
   return it;
 }
 
@@ -94,11 +101,16 @@ __device__ __forceinline__ int64_t next_entry(const BsaArgs& a, const Item& it, 
 // Workgroup = NP groups of BLK/32 waves.  Every group covers all BLK queries
 // of the query block (one wave per 32 queries) and takes every NP-th 64-key
 // tile of the row; the groups' partial softmax states are merged through LDS
-// at the end.  K / V tiles travel global -> LDS with direct (DMA) loads into an
-// S-stage ring, so no registers are spent on staging and the loads of later
-// tiles overlap the MFMAs of the current one.  The row's key-block ids are
-// copied to LDS first, so the loop itself issues no global loads besides the
-// DMA (the explicit vmcnt waits then count only tile loads).
+// at the end.
+//
+// Per group the tiles form a software pipeline: while the softmax of tile n
+// runs on the VALU, the MFMAs of S(n+1) = K(n+1) Q^T are already in flight, and
+// the MFMAs of O += V(n) P(n) overlap the bookkeeping of the next step.  K and
+// V travel global -> LDS by direct (DMA) loads into two rings of S slots; the K
+// ring runs one tile ahead of the V ring, so at step n the slots of K(n+1) and
+// V(n) are read while K(n+S) and V(n+S-1) are in flight.  The row's key-block
+// ids are held in VGPR lanes and read with v_readlane, so the loop issues no
+// memory access besides the DMA and LDS operand reads.
 
 // Workgroup barrier that does not drain outstanding DMA loads (a fenced
 // barrier would wait for every in-flight tile, not just the one needed).
@@ -108,6 +120,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Wait until at most c * J vector loads of this wave are outstanding (c <= 4).
+template <int J>
+__device__ __forceinline__ void wait_vm_units(int c) {
+  switch (c) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<J>(); break;
+    case 2: wait_vmcnt<2 * J>(); break;
+    case 3: wait_vmcnt<3 * J>(); break;
+    default: wait_vmcnt<4 * J>(); break;
+  }
+}
 
 // 16-byte chunk position inside a K row: XOR with the key's low bits so the
 // 32 rows read by one MFMA operand load fall into distinct bank groups.
@@ -115,32 +138,44 @@ __device__ __forceinline__ int swz_k(int c, int key) { return c ^ (key & 7); }
 // ... and inside a V row, matched to the 4-row groups of the transpose read.
 __device__ __forceinline__ int swz_v(int c, int key) { return c ^ ((key & 3) << 1); }
 
-template <int D, int BLK, int NP, int S>
+// Software-pipeline shape: K operand k-steps read ahead, VALU instructions
+// scheduled after each S(n+1) MFMA.
+#ifndef SA_KPRE
+#define SA_KPRE 4
+#endif
+#ifndef SA_VGROUP
+#define SA_VGROUP 12
+#endif
+
+template <int D, int BLK, int NP, int S, bool PIPE>
 struct BsaCfg {
-  static constexpr int QW = BLK / 32;               // waves per group
-  static constexpr int NW = QW * NP;                // waves per workgroup
-  static constexpr int NT = NW * 64;                // threads
-  static constexpr int SUBS = BLK / 64;             // 64-key tiles per key block
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per K / V row
-  static constexpr int ROWB = D * 2;                // bytes per K / V row
-  static constexpr int KVB = 64 * ROWB;             // bytes of one K (or V) tile
-  static constexpr int TILEB = 2 * KVB;             // K + V
-  static constexpr int STAGEB = NP * TILEB;
-  static constexpr int LIST = 256;                  // key-block ids held in LDS at once
-  static constexpr int LDSB = S * STAGEB + LIST * 4;
-  static constexpr int CHUNKS = TILEB / 16;         // 16-byte chunks per tile
-  static constexpr int LPI = NP * CHUNKS / NT;      // DMA loads per thread per stage
-  static_assert(S >= 2 && S <= 3, "2 or 3 stages");
+  static constexpr int QW = BLK / 32;          // waves per group
+  static constexpr int NW = QW * NP;           // waves per workgroup
+  static constexpr int NT = NW * 64;           // threads
+  static constexpr int SUBS = BLK / 64;        // 64-key tiles per key block
+  static constexpr int CPR = D / 8;            // 16-byte chunks per K / V row
+  static constexpr int ROWB = D * 2;           // bytes per K / V row
+  static constexpr int KVB = 64 * ROWB;        // bytes of one K (or V) tile
+  static constexpr int SLOTB = NP * KVB;       // one ring slot: a tile per group
+  static constexpr int VRING = S * SLOTB;      // offset of the V ring
+  static constexpr int LDSB = 2 * S * SLOTB;
+  static constexpr int JN = KVB / 16 / (QW * 64);  // DMA loads per thread per tile
+  // K operand k-steps of the next tile read at the top of a step (the rest
+  // are read inside the MFMA / softmax interleave)
+  static constexpr int KPRE = SA_KPRE < D / 16 ? SA_KPRE : D / 16;
+  static constexpr int KPA = KPRE > 0 ? KPRE : 1;
+  static_assert(S >= 2 && S <= 3, "2 or 3 ring slots");
+  static_assert(JN >= 1 && (KVB / 16) % (QW * 64) == 0, "tiles must split evenly over a group");
+  static_assert(4 * JN < 64, "vmcnt range");
   // merge area: per (group > 0, wave, lane): O^T partial (D/2 floats), m, l
   static constexpr int MERGEB = (NP - 1) * QW * 64 * (D / 2 + 2) * 4;
-  static_assert(MERGEB <= S * STAGEB, "merge area must fit in the ring");
+  static_assert(MERGEB <= LDSB, "merge area must fit in the rings");
 };
 
-template <int D, int BLK, int NP, int S>
+template <int D, int BLK, int NP, int S, bool PIPE>
 __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArgs a) {
-  using C = BsaCfg<D, BLK, NP, S>;
+  using C = BsaCfg<D, BLK, NP, S, PIPE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int32_t* list = (int32_t*)(smem + S * C::STAGEB);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = sa::uniform(tid >> 6);
@@ -155,152 +190,251 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
   const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
   const int32_t limit = a.causal ? it.i + 1 : a.nb;  // usable key blocks are < limit
 
-  // Q^T as the B operand: lane holds query lq of this wave, d = 16 k + 8 hl .. +7
+  // Q^T as the B operand: lane holds query lq of this wave, d = 16 k + 8 hl .. +7.
+  // A negative scale is folded into Q (exact sign flip), so the softmax below
+  // always works with a positive log2 scale.
   const int q_local = wq * 32 + lq;
   const int64_t qpos = (int64_t)it.i * BLK + q_local;
   sa::u32x4 qr[D / 16];
 #pragma unroll
-  for (int k = 0; k < D / 16; ++k) qr[k] = *(const sa::u32x4*)(Q + qpos * a.qs[2] + 16 * k + 8 * hl);
-  // Consume Q here so the compiler's own load wait happens once, before the
-  // loop, and not inside it where it would also wait for the tile prefetch.
+  for (int k = 0; k < D / 16; ++k) {
+    qr[k] = *(const sa::u32x4*)(Q + qpos * a.qs[2] + 16 * k + 8 * hl);
 #pragma unroll
-  for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qr[k]));
+    for (int w = 0; w < 4; ++w) qr[k][w] ^= a.qsign;
+  }
 
   sa::f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
-  float m_used = -INFINITY, l_run = 0.f;
-  const float c2 = a.scale_log2;
-  constexpr float kTau = 8.f;  // rescale only when the running max grows by > 2^8
+  // Running reference max (log2 units).  Finite start: a fully masked tile
+  // then yields exp2(-inf) = 0 instead of inf - inf.
+  float m_used = -1e30f;
+  const float c2 = a.scale_log2;  // > 0
+  constexpr float kTau = 8.f;     // rescale only when the running max grows by > 2^8
 
-  // DMA plan: for each tile of a stage, K and V (KVB bytes each) are copied by
-  // JN wave-instructions per thread; instruction j of wave w covers chunks
-  // [j*NT + 64 w, j*NT + 64 w + 64) of the K (or V) tile, i.e. whole rows.
-  // The lane part of each swizzled source offset is fixed for the kernel.
-  constexpr int JN = (C::CHUNKS / 2) / C::NT;
-  static_assert((C::CHUNKS / 2) % C::NT == 0, "K / V tiles must split evenly over the threads");
-  uint32_t offK[JN], offV[JN];
+  // DMA plan: copy j of wave wq of a group moves chunks [64 (j QW + wq), +64)
+  // of the group's K (or V) tile, i.e. whole rows; lane i lands at 16 i past
+  // the copy's LDS base.  Source offsets are fixed per lane.  When the rows of
+  // a tile are contiguous in global memory (sequence stride = d) and copies
+  // j, j + 1 are 2048 bytes apart in both spaces, they share one M0 setup.
+  uint32_t offK[C::JN], offV[C::JN];
 #pragma unroll
-  for (int j = 0; j < JN; ++j) {
-    const int r = j * C::NT + wave * 64 + lane;  // chunk of this lane
+  for (int j = 0; j < C::JN; ++j) {
+    const int r = (j * C::QW + wq) * 64 + lane;  // chunk of this lane
     const int key = r / C::CPR, cs = r % C::CPR;
     offK[j] = (uint32_t)(key * ks2 * 2) + 16u * (uint32_t)swz_k(cs, key);
     offV[j] = (uint32_t)(key * vs2 * 2) + 16u * (uint32_t)swz_v(cs, key);
   }
+  constexpr bool kPairs = C::QW * 64 * 16 == 2048 && C::JN % 2 == 0;
+  const bool k_contig = kPairs && ks2 == D, v_contig = kPairs && vs2 == D;
+  const uint32_t kring = sa::lds_addr(smem) + grp * C::KVB;
+  const uint32_t vring = kring + C::VRING;
+  const uint8_t* const kring_p = smem + grp * C::KVB;
+  const uint8_t* const vring_p = kring_p + C::VRING;
 
-  for (int64_t base = it.e_beg; base < it.e_end; base += C::LIST) {
-    const int cnt = (int)min((int64_t)C::LIST, it.e_end - base);
-    __syncthreads();  // previous pass finished with the list and the ring
-    for (int x = tid; x < cnt; x += C::NT) list[x] = a.col_idx[base + x];
-    __syncthreads();
-    const int T = cnt * C::SUBS;        // 64-key tiles of this pass
-    const int NI = (T + NP - 1) / NP;   // pipeline iterations
+  // copies of one 64-key tile (key block kb, sub-tile sub) into ring slot m % S
+  auto dma_tile = [&](const uint16_t* X, int64_t xs2, const uint32_t(&off)[C::JN], bool contig,
+                      uint32_t ring, int m, int32_t kb, int sub) {
+    const void* src = X + ((int64_t)kb * BLK + 64 * sub) * xs2;
+    const uint32_t dst = ring + (m % S) * C::SLOTB + wq * 64 * 16;
+    if (contig) {
+#pragma unroll
+      for (int j = 0; j < C::JN; j += 2) sa::dma16x2(src, off[j], dst + j * 2048);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::JN; ++j) sa::dma16(src, off[j], dst + j * C::QW * 64 * 16);
+    }
+  };
 
-    // key block of tile t (t clamped into the pass); ids outside [0, limit)
-    // are replaced by a safe block and the tile is skipped at compute time
-    auto tile_kb = [&](int t, bool& ok) -> int32_t {
-      const int32_t kb = sa::uniform(list[min(t, T - 1) / C::SUBS]);
-      ok = kb >= 0 && kb < limit;
-      return ok ? kb : it.i;
+  sa::f32x16 sA[2], sB[2];
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};  // partial row sums (l = their total)
+  bool first_pass = true;
+  for (int64_t base = it.e_beg; base < it.e_end; base += 64) {
+    const int cnt = (int)min((int64_t)64, it.e_end - base);
+    // key-block ids of the pass, entry x in lane x
+    const int lst = lane < cnt ? a.col_idx[base + lane] : -1;
+    // Q and the list are consumed here, before any copy is in flight, so the
+    // compiler's own load waits never stall on a tile.
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) sa::keep(qr[k]);
+    sa::keep(lst);
+    if (!first_pass) ring_barrier();  // every wave is done with the rings
+    first_pass = false;
+
+    const int T = cnt * C::SUBS;       // 64-key tiles of this pass
+    const int NI = (T + NP - 1) / NP;  // pipeline steps of each group
+
+    // Key block of this group's tile at step m, or -1 when the tile is past
+    // the end of the pass or its id is outside [0, limit) (such tiles are
+    // loaded from a safe block and fully masked).
+    auto tile_kb = [&](int m) -> int32_t {
+      const int t = m * NP + grp;
+      const int32_t kb = sa::readlane(lst, min(t, T - 1) / C::SUBS);
+      return (t < T && (uint32_t)kb < (uint32_t)limit) ? kb : -1;
+    };
+    auto tile_sub = [&](int m) -> int { return C::SUBS == 1 ? 0 : min(m * NP + grp, T - 1) % C::SUBS; };
+    auto dma_k = [&](int m, int32_t kb) {
+      dma_tile(K, ks2, offK, k_contig, kring, m, kb < 0 ? it.i : kb, tile_sub(m));
+    };
+    auto dma_v = [&](int m, int32_t kb) {
+      dma_tile(V, vs2, offV, v_contig, vring, m, kb < 0 ? it.i : kb, tile_sub(m));
+    };
+    // K operand of S^T = K Q^T for k-step k: 32 keys (kt) x 16 dims.
+    auto k_operand = [&](const uint8_t* ks, int k, int kt) -> sa::u32x4 {
+      const int key = 32 * kt + lq;
+      return *(const sa::u32x4*)(ks + key * C::ROWB + swz_k(2 * k + hl, key) * 16);
     };
 
-    auto issue_stage = [&](int n) {  // DMA loads of iteration n into stage n % S
-      uint8_t* st = smem + (n % S) * C::STAGEB;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        bool ok;
-        const int t = min(n * NP + p, T - 1);
-        const int64_t key0 = (int64_t)tile_kb(t, ok) * BLK + 64 * (t % C::SUBS);
-        const char* kbase = (const char*)(K + key0 * ks2);
-        const char* vbase = (const char*)(V + key0 * vs2);
-        uint8_t* kdst = st + p * C::TILEB + wave * 64 * 16;
-#pragma unroll
-        for (int j = 0; j < JN; ++j) {
-          // wave-uniform LDS base; lane i lands at base + 16 i
-          sa::dma16(kbase + offK[j], kdst + j * C::NT * 16);
-          sa::dma16(vbase + offV[j], kdst + C::KVB + j * C::NT * 16);
-        }
-      }
-    };
-
-    if (NI > 0) issue_stage(0);
-    if (S == 3 && NI > 1) issue_stage(1);
-
-    for (int n = 0; n < NI; ++n) {
-      if (S == 3 && n + 1 < NI)
-        wait_vmcnt<C::LPI>();
-      else
-        wait_vmcnt<0>();
-      ring_barrier();  // stage n is complete for every wave; stage n-1 is free
-      if (n + S - 1 < NI) issue_stage(n + S - 1);
-
-      const int t = n * NP + grp;
-      bool ok;
-      const int32_t kb = tile_kb(t, ok);
-      const int sub = t % C::SUBS;
-      const bool diag = a.causal && kb == it.i;
-      const int sub_local = 64 * sub;
-      if (!(t < T && ok && !(diag && sub_local > wq * 32 + 31))) continue;
-
-      const uint8_t* Ks = smem + (n % S) * C::STAGEB + grp * C::TILEB;
-      const uint8_t* Vs = Ks + C::KVB;
-      // S^T = K Q^T for 64 keys x 32 queries
-      sa::f32x16 sacc[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
+    auto qk = [&](const uint8_t* ks, sa::f32x16(&dst)[2]) {
 #pragma unroll
       for (int k = 0; k < D / 16; ++k)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int key = 32 * kt + lq;
-          const sa::u32x4 av = *(const sa::u32x4*)(Ks + key * C::ROWB + swz_k(2 * k + hl, key) * 16);
-          sacc[kt] = sa::mfma32(av, qr[k], sacc[kt]);
+        for (int kt = 0; kt < 2; ++kt)
+          dst[kt] = k == 0 ? sa::mfma32_z(k_operand(ks, k, kt), qr[k])
+                           : sa::mfma32(k_operand(ks, k, kt), qr[k], dst[kt]);
+    };
+
+    // Key blocks of the tiles whose copies are in flight (q0 = step n).
+    int32_t q0 = tile_kb(0), q1 = NI > 1 ? tile_kb(1) : -1, q2 = S > 2 && NI > 2 ? tile_kb(2) : -1;
+    if constexpr (PIPE) {
+      // prologue: K(0), then {K(j), V(j-1)} for j < S; S(0) = K(0) Q^T
+      dma_k(0, q0);
+      if (1 < NI) dma_k(1, q1);
+      dma_v(0, q0);
+      if (S > 2) {
+        if (2 < NI) dma_k(2, q2);
+        if (1 < NI) dma_v(1, q1);
+      }
+      int c = 0;
+#pragma unroll
+      for (int j = 1; j < S; ++j) c += (j < NI) + (j - 1 < NI);
+      wait_vm_units<C::JN>(c);
+      ring_barrier();
+      qk(kring_p, sA);
+    } else {
+      // prologue: {K(j), V(j)} for j < S - 1
+      dma_k(0, q0);
+      dma_v(0, q0);
+      if (S > 2 && 1 < NI) {
+        dma_k(1, q1);
+        dma_v(1, q1);
+      }
+    }
+
+    // One pipeline step: softmax + O update of tile n (logits in `cur`), and,
+    // when NEXT, the logits of tile n + 1 into `nxt`.
+    auto step = [&](int n, sa::f32x16(&cur)[2], sa::f32x16(&nxt)[2], auto next_tag) {
+      constexpr bool NEXT = decltype(next_tag)::value;
+      SA_SCHED_BARRIER();  // the previous step's MFMAs are issued before this wait
+      int32_t qn = -1;  // key block of the newest tile put in flight
+      if constexpr (PIPE) {
+        // K(n+1) and V(n) must have landed (all waves): wait for the copies
+        // issued up to step n+1-S; the barrier then also frees K(n), V(n-1).
+        if (S == 3)
+          wait_vm_units<C::JN>((n + 2 < NI) + (n + 1 < NI));
+        else
+          wait_vmcnt<0>();
+        ring_barrier();
+        if (n + S < NI) {
+          qn = tile_kb(n + S);
+          dma_k(n + S, qn);
         }
-      // Diagonal tile: keys after the query are replaced by a logit that
-      // scales to -inf (the sign of c2 picks it; c2 is never 0), so the common
-      // path below needs no per-element select.
-      if (diag && (sub_local + 63 > wq * 32)) {
-        const float masked = c2 > 0.f ? -INFINITY : INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key_local = sub_local + 32 * kt + 8 * (e >> 2) + 4 * hl + (e & 3);
-            if (key_local > q_local) sacc[kt][e] = masked;
-          }
-      }
-      // tile max of the scaled logits (log2 units) over both half-rows
-      float r;
-      if (c2 > 0.f) {
-        r = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) r = fmaxf(r, sacc[kt][e]);
-        r = fmaxf(r, __shfl_xor(r, 32));
+        if (n + S - 1 < NI) dma_v(n + S - 1, S > 2 ? q2 : q1);
       } else {
-        r = INFINITY;
+        // K(n) and V(n) must have landed; the barrier also frees tile n-1
+        if (S == 3)
+          wait_vm_units<C::JN>(2 * (n + 1 < NI));
+        else
+          wait_vmcnt<0>();
+        ring_barrier();
+        if (n + S - 1 < NI) {
+          qn = tile_kb(n + S - 1);
+          dma_k(n + S - 1, qn);
+          dma_v(n + S - 1, qn);
+        }
+        qk(kring_p + (n % S) * C::SLOTB, cur);
+      }
+
+      const uint8_t* ks = kring_p + ((n + 1) % S) * C::SLOTB;  // K(n+1) (PIPE only)
+      const uint8_t* vs = vring_p + (n % S) * C::SLOTB;
+      sa::u32x4 kop[C::KPA][2];
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int k = 0; k < C::KPRE; ++k)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) kop[k][kt] = k_operand(ks, k, kt);
+      }
+
+      // masking of tile n: the diagonal block (keys after the query) and
+      // skipped tiles (everything) get -inf logits
+      const int32_t kb = q0;
+      const int sub_local = 64 * tile_sub(n);
+      if (kb < 0 || (a.causal && kb == it.i && sub_local + 63 > wq * 32)) {
+        // element (kt, e) holds key 32 kt + 8 (e / 4) + 4 hl + e % 4 of the tile
+        const int lim = (kb < 0 ? -1 : q_local - sub_local) - 4 * hl;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) r = fminf(r, sacc[kt][e]);
-        r = fminf(r, __shfl_xor(r, 32));
+          for (int e = 0; e < 16; ++e)
+            cur[kt][e] = 32 * kt + 8 * (e >> 2) + (e & 3) > lim ? -INFINITY : cur[kt][e];
       }
-      const float m_tile = r * c2;
+      // advance the key-block queue
+      if constexpr (PIPE) {
+        q0 = q1;
+        if (S > 2) {
+          q1 = q2;
+          q2 = qn;
+        } else {
+          q1 = qn;
+        }
+      } else {
+        if (S > 2) {
+          q0 = q1;
+          q1 = qn;
+        } else {
+          q0 = qn;
+        }
+      }
+
+      // tile max over both half-rows, in log2 units (max3 chains)
+      float r[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const sa::f32x16& x = cur[c >> 1];
+        const int o = 8 * (c & 1);
+        float v = fmaxf(fmaxf(x[o], x[o + 1]), x[o + 2]);
+        v = fmaxf(fmaxf(v, x[o + 3]), x[o + 4]);
+        r[c] = fmaxf(fmaxf(v, x[o + 5]), x[o + 6]);
+      }
+      float rm = fmaxf(fmaxf(r[0], r[1]), r[2]);
+      rm = fmaxf(fmaxf(rm, r[3]), cur[0][7]);
+      rm = fmaxf(fmaxf(rm, cur[0][15]), cur[1][7]);
+      rm = sa::max_xor32(fmaxf(rm, cur[1][15]));
+      const float m_tile = rm * c2;
       const bool need = m_tile > m_used + kTau;
       if (__ballot(need)) {  // some query's max grew: move its reference
         const float m_new = need ? m_tile : m_used;
         const float alpha = sa::fast_exp2(m_used - m_new);
-        l_run *= alpha;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ls[w] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
         m_used = m_new;
+      }
+
+      // S(n+1) MFMAs (issued first, they run while the VALU works on P(n))
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const sa::u32x4 av = k < C::KPRE ? kop[k < C::KPRE ? k : 0][kt] : k_operand(ks, k, kt);
+            nxt[kt] = k == 0 ? sa::mfma32_z(av, qr[k]) : sa::mfma32(av, qr[k], nxt[kt]);
+          }
       }
       // P = exp2(s c - m) packed to bf16 as the B operand of O^T += V^T P^T
       sa::u32x4 pb[4];
@@ -311,16 +445,14 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const int e = 8 * h2 + 2 * w;
-            pb[2 * kt + h2][w] = sa::pack_bf16x2(sa::fast_exp2(__builtin_fmaf(sacc[kt][e], c2, -m_used)),
-                                                 sa::fast_exp2(__builtin_fmaf(sacc[kt][e + 1], c2, -m_used)));
+            pb[2 * kt + h2][w] = sa::pack_bf16x2(sa::fast_exp2(__builtin_fmaf(cur[kt][e], c2, -m_used)),
+                                                 sa::fast_exp2(__builtin_fmaf(cur[kt][e + 1], c2, -m_used)));
           }
-      // row sum over the rounded P actually fed to the MFMA
-      float lsum = 0.f;
+      // row sums over the rounded P actually fed to the MFMA
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) lsum = sa::dot2_bf16(pb[u][w], 0x3f803f80u, lsum);
-      l_run += lsum;
+        for (int w = 0; w < 4; ++w) ls[w] = sa::dot2_bf16(pb[u][w], 0x3f803f80u, ls[w]);
       // O^T += V^T P^T; the V^T operand comes from transpose reads of row-major V
       const int gi = lane >> 4, ii = lane & 15;
 #pragma unroll
@@ -331,20 +463,51 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
         for (int u = 0; u < 4; ++u) {
           const int keyA = 16 * u + 4 * hl + (ii >> 2);
           const int keyB = keyA + 8;
-          const sa::u32x2 l2 = sa::lds_read_tr16(Vs + keyA * C::ROWB + swz_v(cs, keyA) * 16 + half * 8);
-          const sa::u32x2 h2 = sa::lds_read_tr16(Vs + keyB * C::ROWB + swz_v(cs, keyB) * 16 + half * 8);
+          const sa::u32x2 l2 = sa::lds_read_tr16(vs + keyA * C::ROWB + swz_v(cs, keyA) * 16 + half * 8);
+          const sa::u32x2 h2 = sa::lds_read_tr16(vs + keyB * C::ROWB + swz_v(cs, keyB) * 16 + half * 8);
           const sa::u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
           oacc[dt] = sa::mfma32(av, pb[u], oacc[dt]);
         }
       }
+      // issue pattern: V operand reads first, then each S(n+1) MFMA followed by
+      // a slice of the softmax VALU work, then the O MFMAs
+      SA_SCHED_GROUP(0x100, 2 * (D / 32) * 4 + (NEXT ? 2 * (D / 16 - C::KPRE) : 0));
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int x = 0; x < 2 * (D / 16); ++x) {
+          SA_SCHED_GROUP(0x008, 1);
+          SA_SCHED_GROUP(0x002, SA_VGROUP);
+        }
+      }
+      SA_SCHED_GROUP(0x002, 128);
+      SA_SCHED_GROUP(0x008, 4 * (D / 32));
+    };
+
+    using yes = std::true_type;
+    using no = std::false_type;
+    if constexpr (PIPE) {
+      int n = 0;
+      for (; n + 2 < NI; n += 2) {
+        step(n, sA, sB, yes{});
+        step(n + 1, sB, sA, yes{});
+      }
+      if (n + 1 < NI) {
+        step(n, sA, sB, yes{});
+        step(n + 1, sB, sA, no{});
+      } else {
+        step(n, sA, sB, no{});
+      }
+    } else {
+      for (int n = 0; n < NI; ++n) step(n, sA, sB, no{});
     }
   }
+  float l_run = (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
   // merge the groups' partial states into group 0
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sa::sum_xor32(l_run);
   if constexpr (NP > 1) {
     wait_vmcnt<0>();
-    __syncthreads();  // every wave is done with the ring; reuse it
+    __syncthreads();  // every wave is done with the rings; reuse them
     float* mg = (float*)smem;
     constexpr int PER = D / 2 + 2;
     if (grp > 0) {
@@ -363,8 +526,7 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
       const float* slot = mg + (((g - 1) * C::QW + wq) * 64 + lane) * PER;
       const float mo = slot[D / 2], lo = slot[D / 2 + 1];
       const float mm = fmaxf(m_used, mo);
-      const float ms = mm == -INFINITY ? 0.f : mm;
-      const float a0 = sa::fast_exp2(m_used - ms), a1 = sa::fast_exp2(mo - ms);
+      const float a0 = sa::fast_exp2(m_used - mm), a1 = sa::fast_exp2(mo - mm);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -465,18 +627,19 @@ sa_status launch(Kern kern, const BsaArgs& a, int threads, int lds_bytes, hipStr
   return sa_host::check_launch(name);
 }
 
-// (groups per workgroup NP, ring stages S) of each compiled tile shape
+// (groups per workgroup NP, ring slots S, software-pipelined S(n+1)) of each
+// compiled tile shape
 #ifndef SA_CFG_64_64
-#define SA_CFG_64_64 1, 2
+#define SA_CFG_64_64 1, 2, true
 #endif
 #ifndef SA_CFG_64_128
-#define SA_CFG_64_128 1, 2
+#define SA_CFG_64_128 1, 2, true
 #endif
 #ifndef SA_CFG_128_64
-#define SA_CFG_128_64 1, 2
+#define SA_CFG_128_64 1, 2, false
 #endif
 #ifndef SA_CFG_128_128
-#define SA_CFG_128_128 1, 2
+#define SA_CFG_128_128 1, 2, false
 #endif
 
 // The kernel must be named in a non-template context for its host stub to be
@@ -529,6 +692,9 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   sa_host::Strides st[4];
   const sa_status ss = sa_host::resolve_strides(strides, B, H, H_kv, N, d, dtype == SA_BF16 ? 8 : 4, st);
   if (ss != SA_OK) return ss;
+  // the bf16 kernel keeps the byte offsets of the rows of a 64-key tile in 32 bits
+  if (dtype == SA_BF16 && (st[1].s >= (int64_t)1 << 24 || st[2].s >= (int64_t)1 << 24))
+    return SA_ERR_UNSUPPORTED;
 
   BsaArgs a = {};
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
@@ -541,7 +707,8 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   a.scale = scale;
   // A zero scale (uniform weights) is run as a tiny positive one: every logit
   // then rounds to 0 exactly as before, while masked logits still scale to -inf.
-  a.scale_log2 = scale != 0.f ? scale * sa::kLog2e : 1e-30f;
+  a.scale_log2 = scale != 0.f ? fabsf(scale) * sa::kLog2e : 1e-30f;
+  a.qsign = scale < 0.f ? 0x80008000u : 0u;
 
   if (dtype == SA_BF16) {
     if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG_64_64, "bsa_fwd_bf16<64,64>");

@@ -39,6 +39,12 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// D(32x32 f32) = A(32x16 bf16) * B(16x32 bf16) (zero accumulator, an inline constant).
+__device__ __forceinline__ f32x16 mfma32_z(u32x4 a, u32x4 b) {
+  const f32x16 z = {};
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), z, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014): advance by the
@@ -57,22 +63,77 @@ __device__ __forceinline__ int wave_lane() { return __lane_id(); }
 // pass, and its launch stub would be missing.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
-// (lds_base must be the same for the whole wave).  Issued as inline asm so the
-// compiler does not track it: it would otherwise wait for every outstanding
-// DMA before any later LDS read, which serialises a multi-stage ring.  The
-// caller orders the DMA with explicit "s_waitcnt vmcnt" + barrier.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-  uint32_t saved;  // M0 is restored so code around the asm may keep using it
+// Value of x in lane `src` (wave-uniform result, no memory access).
+__device__ __forceinline__ int readlane(int x, int src) { return __builtin_amdgcn_readlane(x, src); }
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Direct global -> LDS copies (global_load_lds_dwordx4): each lane's 16 bytes
+// from sbase + voff land at M0 + 16 * lane (M0 = wave-uniform LDS address).
+// Issued as inline asm so the compiler does not track them: it would otherwise
+// wait for every outstanding copy before any later LDS read, which serialises
+// a multi-stage ring.  The caller orders them with explicit "s_waitcnt vmcnt"
+// and a barrier.  The instruction offset is added to both the global and the
+// LDS address.  M0 is restored, so code around the asm may keep using it; one
+// wait state separates the M0 write from the copy (GFX9 M0 -> LDS-DMA hazard).
+// The asm is device-only: kernel templates that use these helpers must still
+// instantiate in the host pass.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
+#endif
+}
+// Two copies 2048 bytes apart in both spaces (rows that are contiguous in
+// global memory and in LDS).
+__device__ __forceinline__ void dma16x2(const void* sbase, uint32_t voff, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+#endif
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Keep a value live in registers at this point (forces pending loads of it to
+// complete here).
+__device__ __forceinline__ void keep(const u32x4& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+__device__ __forceinline__ void keep(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
 }
 
 // Transpose read of 4 x 16-bit values: within each group of 16 lanes, lane i
@@ -85,3 +146,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
 }
 
 }  // namespace sa
+
+// Instruction-scheduling hint for the device pass: the next `n` instructions of
+// the kind in `mask` (0x2 VALU, 0x8 MFMA, 0x100 LDS read) form one group of the
+// pattern the scheduler must follow within the current basic block.
+// SA_SCHED_BARRIER: no instruction is moved across this point.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define SA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+#define SA_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
+#else
+#define SA_SCHED_GROUP(mask, n)
+#define SA_SCHED_BARRIER()
+#endif
