@@ -64,11 +64,9 @@ struct Item {
   bool ok;
 };
 
-__device__ __forceinline__ Item work_item(const BsaArgs& a) {
+// Work item of head bh = b * H + h at launch position pos of its mask group.
+__device__ __forceinline__ Item work_item_at(const BsaArgs& a, int32_t bh, int32_t pos) {
   Item it;
-  const int32_t BH = a.B * a.H;
-  const int32_t w = blockIdx.x;
-  const int32_t pos = w / BH, bh = w - pos * BH;
   it.b = bh / a.H;
   it.h = bh - it.b * a.H;
   it.kvh = it.h / (a.H / a.H_kv);
@@ -84,6 +82,13 @@ __device__ __forceinline__ Item work_item(const BsaArgs& a) {
   it.e_beg = sa::uniform((int32_t)e0);
   it.e_end = sa::uniform((int32_t)e1);
   return it;
+}
+
+// One row per workgroup: blockIdx = pos * (B * H) + bh.
+__device__ __forceinline__ Item work_item(const BsaArgs& a) {
+  const int32_t BH = a.B * a.H;
+  const int32_t pos = blockIdx.x / BH;
+  return work_item_at(a, blockIdx.x - pos * BH, pos);
 }
 
 // First CSR entry at or after e whose block is usable (in range, and not after
@@ -181,6 +186,7 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
   const int wave = sa::uniform(tid >> 6);
   const int grp = wave / C::QW, wq = wave % C::QW;
   const int hl = lane >> 5, lq = lane & 31;
+
   const Item it = work_item(a);
   if (!it.ok) return;
 
@@ -215,36 +221,44 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
   constexpr float kTau = 8.f;     // rescale only when the running max grows by > 2^8
 
   // DMA plan: copy j of wave wq of a group moves chunks [64 (j QW + wq), +64)
-  // of the group's K (or V) tile, i.e. whole rows; lane i lands at 16 i past
-  // the copy's LDS base.  Source offsets are fixed per lane.  When the rows of
-  // a tile are contiguous in global memory (sequence stride = d) and copies
-  // j, j + 1 are 2048 bytes apart in both spaces, they share one M0 setup.
-  uint32_t offK[C::JN], offV[C::JN];
-#pragma unroll
-  for (int j = 0; j < C::JN; ++j) {
-    const int r = (j * C::QW + wq) * 64 + lane;  // chunk of this lane
+  // of the group's K (or V) tile, i.e. whole rows (RPC rows per copy); lane i
+  // lands at 16 i past the copy's LDS base.  Copy j reads rows RPC j further
+  // down than copy 0, with the same swizzle (RPC is a multiple of 8), so one
+  // per-lane source offset serves every copy.  When the rows of a tile are
+  // contiguous in global memory (sequence stride = d) and copies j, j + 1 are
+  // 2048 bytes apart in both spaces, they share one M0 setup.
+  constexpr int RPC = C::QW * 64 / C::CPR;  // rows per copy
+  static_assert(RPC % 8 == 0, "copies must keep the row swizzle");
+  uint32_t offK, offV;
+  {
+    const int r = wq * 64 + lane;  // chunk of this lane in copy 0
     const int key = r / C::CPR, cs = r % C::CPR;
-    offK[j] = (uint32_t)(key * ks2 * 2) + 16u * (uint32_t)swz_k(cs, key);
-    offV[j] = (uint32_t)(key * vs2 * 2) + 16u * (uint32_t)swz_v(cs, key);
+    offK = (uint32_t)(key * ks2 * 2) + 16u * (uint32_t)swz_k(cs, key);
+    offV = (uint32_t)(key * vs2 * 2) + 16u * (uint32_t)swz_v(cs, key);
   }
-  constexpr bool kPairs = C::QW * 64 * 16 == 2048 && C::JN % 2 == 0;
+  constexpr bool kPairs = C::QW * 64 * 16 == 2048 && C::JN % 4 == 0;
   const bool k_contig = kPairs && ks2 == D, v_contig = kPairs && vs2 == D;
   const uint32_t kring = sa::lds_addr(smem) + grp * C::KVB;
   const uint32_t vring = kring + C::VRING;
   const uint8_t* const kring_p = smem + grp * C::KVB;
   const uint8_t* const vring_p = kring_p + C::VRING;
 
-  // copies of one 64-key tile (key block kb, sub-tile sub) into ring slot m % S
-  auto dma_tile = [&](const uint16_t* X, int64_t xs2, const uint32_t(&off)[C::JN], bool contig,
-                      uint32_t ring, int m, int32_t kb, int sub) {
-    const void* src = X + ((int64_t)kb * BLK + 64 * sub) * xs2;
-    const uint32_t dst = ring + (m % S) * C::SLOTB + wq * 64 * 16;
-    if (contig) {
+  // Copies of one 64-key tile (key block kb >= 0, sub-tile sub) into a ring
+  // slot.  Byte offsets of a block are below 2^32 (the host bounds the
+  // sequence strides), so a 32 x 32-bit product locates the tile.
+  const uint32_t kbs = (uint32_t)(BLK * ks2 * 2), vbs = (uint32_t)(BLK * vs2 * 2);  // bytes per key block
+  const uint32_t offK4 = offK + 4096u, offV4 = offV + 4096u;
+  auto dma_tile = [&](const uint16_t* X, uint32_t xbs, int64_t xs2, uint32_t off, uint32_t off4, bool contig,
+                      uint32_t ring, int slot, int32_t kb, int sub) {
+    const char* src = (const char*)X + (uint64_t)(uint32_t)kb * xbs + (uint32_t)(sub * 64 * xs2 * 2);
+    const uint32_t dst = ring + slot * C::SLOTB + wq * 64 * 16;
+    if (contig) {  // pairs 2048 bytes apart, two pairs per M0 save
 #pragma unroll
-      for (int j = 0; j < C::JN; j += 2) sa::dma16x2(src, off[j], dst + j * 2048);
+      for (int j = 0; j < C::JN; j += 4) sa::dma16x4p(src + j * 2048, off, off4, dst + j * 2048);
     } else {
 #pragma unroll
-      for (int j = 0; j < C::JN; ++j) sa::dma16(src, off[j], dst + j * C::QW * 64 * 16);
+      for (int j = 0; j < C::JN; ++j)
+        sa::dma16(src + (uint64_t)j * RPC * xs2 * 2, off, dst + j * C::QW * 64 * 16);
     }
   };
 
@@ -275,11 +289,11 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
       return (t < T && (uint32_t)kb < (uint32_t)limit) ? kb : -1;
     };
     auto tile_sub = [&](int m) -> int { return C::SUBS == 1 ? 0 : min(m * NP + grp, T - 1) % C::SUBS; };
-    auto dma_k = [&](int m, int32_t kb) {
-      dma_tile(K, ks2, offK, k_contig, kring, m, kb < 0 ? it.i : kb, tile_sub(m));
+    auto dma_k = [&](int m, int32_t kb, int slot) {
+      dma_tile(K, kbs, ks2, offK, offK4, k_contig, kring, slot, kb < 0 ? it.i : kb, tile_sub(m));
     };
-    auto dma_v = [&](int m, int32_t kb) {
-      dma_tile(V, vs2, offV, v_contig, vring, m, kb < 0 ? it.i : kb, tile_sub(m));
+    auto dma_v = [&](int m, int32_t kb, int slot) {
+      dma_tile(V, vbs, vs2, offV, offV4, v_contig, vring, slot, kb < 0 ? it.i : kb, tile_sub(m));
     };
     // K operand of S^T = K Q^T for k-step k: 32 keys (kt) x 16 dims.
     auto k_operand = [&](const uint8_t* ks, int k, int kt) -> sa::u32x4 {
@@ -300,12 +314,12 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
     int32_t q0 = tile_kb(0), q1 = NI > 1 ? tile_kb(1) : -1, q2 = S > 2 && NI > 2 ? tile_kb(2) : -1;
     if constexpr (PIPE) {
       // prologue: K(0), then {K(j), V(j-1)} for j < S; S(0) = K(0) Q^T
-      dma_k(0, q0);
-      if (1 < NI) dma_k(1, q1);
-      dma_v(0, q0);
+      dma_k(0, q0, 0);
+      if (1 < NI) dma_k(1, q1, 1);
+      dma_v(0, q0, 0);
       if (S > 2) {
-        if (2 < NI) dma_k(2, q2);
-        if (1 < NI) dma_v(1, q1);
+        if (2 < NI) dma_k(2, q2, 2 % S);
+        if (1 < NI) dma_v(1, q1, 1);
       }
       int c = 0;
 #pragma unroll
@@ -315,18 +329,22 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
       qk(kring_p, sA);
     } else {
       // prologue: {K(j), V(j)} for j < S - 1
-      dma_k(0, q0);
-      dma_v(0, q0);
+      dma_k(0, q0, 0);
+      dma_v(0, q0, 0);
       if (S > 2 && 1 < NI) {
-        dma_k(1, q1);
-        dma_v(1, q1);
+        dma_k(1, q1, 1);
+        dma_v(1, q1, 1);
       }
     }
 
     // One pipeline step: softmax + O update of tile n (logits in `cur`), and,
     // when NEXT, the logits of tile n + 1 into `nxt`.
-    auto step = [&](int n, sa::f32x16(&cur)[2], sa::f32x16(&nxt)[2], auto next_tag) {
+    auto step = [&](int n, sa::f32x16(&cur)[2], sa::f32x16(&nxt)[2], auto next_tag, auto par_tag) {
       constexpr bool NEXT = decltype(next_tag)::value;
+      // ring slot of tile n (a compile-time constant when the caller passes
+      // the parity of n and there are two slots)
+      constexpr int PAR = decltype(par_tag)::value;
+      const int pn = S == 2 && PAR >= 0 ? PAR : n % S;
       SA_SCHED_BARRIER();  // the previous step's MFMAs are issued before this wait
       int32_t qn = -1;  // key block of the newest tile put in flight
       if constexpr (PIPE) {
@@ -339,9 +357,9 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
         ring_barrier();
         if (n + S < NI) {
           qn = tile_kb(n + S);
-          dma_k(n + S, qn);
+          dma_k(n + S, qn, pn);
         }
-        if (n + S - 1 < NI) dma_v(n + S - 1, S > 2 ? q2 : q1);
+        if (n + S - 1 < NI) dma_v(n + S - 1, S > 2 ? q2 : q1, (pn + S - 1) % S);
       } else {
         // K(n) and V(n) must have landed; the barrier also frees tile n-1
         if (S == 3)
@@ -351,14 +369,14 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
         ring_barrier();
         if (n + S - 1 < NI) {
           qn = tile_kb(n + S - 1);
-          dma_k(n + S - 1, qn);
-          dma_v(n + S - 1, qn);
+          dma_k(n + S - 1, qn, (pn + S - 1) % S);
+          dma_v(n + S - 1, qn, (pn + S - 1) % S);
         }
-        qk(kring_p + (n % S) * C::SLOTB, cur);
+        qk(kring_p + pn * C::SLOTB, cur);
       }
 
-      const uint8_t* ks = kring_p + ((n + 1) % S) * C::SLOTB;  // K(n+1) (PIPE only)
-      const uint8_t* vs = vring_p + (n % S) * C::SLOTB;
+      const uint8_t* ks = kring_p + ((pn + 1) % S) * C::SLOTB;  // K(n+1) (PIPE only)
+      const uint8_t* vs = vring_p + pn * C::SLOTB;
       sa::u32x4 kop[C::KPA][2];
       if constexpr (NEXT) {
 #pragma unroll
@@ -485,20 +503,22 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
 
     using yes = std::true_type;
     using no = std::false_type;
+    using even = std::integral_constant<int, 0>;
+    using odd = std::integral_constant<int, 1>;
+    int n = 0;
     if constexpr (PIPE) {
-      int n = 0;
       for (; n + 2 < NI; n += 2) {
-        step(n, sA, sB, yes{});
-        step(n + 1, sB, sA, yes{});
+        step(n, sA, sB, yes{}, even{});
+        step(n + 1, sB, sA, yes{}, odd{});
       }
       if (n + 1 < NI) {
-        step(n, sA, sB, yes{});
-        step(n + 1, sB, sA, no{});
+        step(n, sA, sB, yes{}, even{});
+        step(n + 1, sB, sA, no{}, odd{});
       } else {
-        step(n, sA, sB, no{});
+        step(n, sA, sB, no{}, even{});
       }
     } else {
-      for (int n = 0; n < NI; ++n) step(n, sA, sB, no{});
+      for (; n < NI; ++n) step(n, sA, sB, no{}, std::integral_constant<int, -1>{});
     }
   }
   float l_run = (ls[0] + ls[1]) + (ls[2] + ls[3]);

@@ -118,6 +118,48 @@ __device__ __forceinline__ void dma16x2(const void* sbase, uint32_t voff, uint32
 #endif
 }
 
+// Four copies of 2048-byte-spaced pairs: copies at (off, lds), (off + 2048,
+// lds + 2048), (off4k, lds + 4096), (off4k + 2048, lds + 6144), where off4k =
+// off + 4096 (one M0 save / restore for the four).
+__device__ __forceinline__ void dma16x4p(const void* sbase, uint32_t off, uint32_t off4k, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:2048\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "global_load_lds_dwordx4 %2, %3 offset:2048\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "v"(off4k), "s"(sbase), "s"(lds), "s"(lds + 4096u)
+      : "memory");
+#endif
+}
+
+// Four copies 1024 bytes apart in both spaces.
+__device__ __forceinline__ void dma16x4(const void* sbase, uint32_t voff, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:1024\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:2048\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+#endif
+}
+
 // LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
