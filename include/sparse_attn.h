@@ -144,6 +144,26 @@ sa_status sparse_attn_build_mask(const sa_mask_desc* desc, int32_t* row_ptr, int
                                  int64_t col_capacity, int32_t* sched, hipStream_t stream);
 
 /*
+ * Literal flags from byte content (compression paper, Sec. 3.1, Eq. 1-2;
+ * Appendix B, Algorithm 1 steps 1-2).  Host only: no GPU work.
+ * Each of G sequences of n_bytes bytes is cut into B = n_bytes / block_bytes
+ * blocks; c_i = size in bytes of block i compressed on its own by gzip at
+ * `level` (zlib deflate, gzip container, window 15, memory level 8, default
+ * strategy); block i is literal iff c_i * B > sum_j c_j, i.e. its compression
+ * ratio c_i / block_bytes is above the sequence mean.
+ *   bytes      HOST uint8 [G][n_bytes]
+ *   flags_out  HOST uint8 [G][B] (1 = literal); copy to the device to use as
+ *              sa_mask_desc.literal_flags
+ *   sizes_out  HOST int32 [G][B] or NULL: the compressed sizes c_i
+ *   level      1..9 (the paper uses 1)
+ * SA_ERR_INVALID if n_bytes % block_bytes != 0 or a size is out of range;
+ * SA_ERR_UNSUPPORTED if B > SA_MAX_BLOCKS; argument errors return before
+ * anything is written.
+ */
+sa_status sparse_attn_literal_flags(const uint8_t* bytes, int32_t G, int64_t n_bytes, int32_t block_bytes,
+                                    int32_t level, uint8_t* flags_out, int32_t* sizes_out);
+
+/*
  * Block-sparse attention forward.
  *
  * For token t in query block qb = t / block of (b, h), with mask row

@@ -14,5 +14,6 @@ from .api import (  # noqa: F401
     sparse_attn_build_mask,
     sparse_attn_check_mask_desc,
     sparse_attn_fwd,
+    sparse_attn_literal_flags,
     sparse_attn_mask_capacity,
 )

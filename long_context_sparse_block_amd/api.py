@@ -162,6 +162,28 @@ def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_st
     return o, lse_t
 
 
+def sparse_attn_literal_flags(data, block_bytes, level=1):
+    """Literal flags of byte sequences by per-block gzip size (C, host only).
+
+    ``data``: bytes (one sequence) or a uint8 numpy array [G, n_bytes].
+    Returns (flags uint8 [G, B], sizes int32 [G, B]) as numpy arrays.
+    """
+    import numpy as np
+    arr = np.frombuffer(data, dtype=np.uint8)[None, :] if isinstance(data, (bytes, bytearray)) else np.asarray(data)
+    if arr.dtype != np.uint8 or arr.ndim != 2:
+        raise ValueError("data must be bytes or a uint8 array [G, n_bytes]")
+    arr = np.ascontiguousarray(arr)
+    G, n = arr.shape
+    nb = n // int(block_bytes) if block_bytes > 0 else 0
+    flags = np.zeros((G, max(nb, 1)), dtype=np.uint8)
+    sizes = np.zeros((G, max(nb, 1)), dtype=np.int32)
+    st = L.lib().sparse_attn_literal_flags(arr.ctypes.data_as(ctypes.c_void_p), G, n, int(block_bytes),
+                                           int(level), flags.ctypes.data_as(ctypes.c_void_p),
+                                           sizes.ctypes.data_as(ctypes.c_void_p))
+    _check(st, "sparse_attn_literal_flags")
+    return flags[:, :nb], sizes[:, :nb]
+
+
 def fibonacci_base(limit):
     """1, 2, 3, 5, 8, ... below ``limit`` (the rung base of the offset pattern)."""
     out, a, b = [], 1, 2

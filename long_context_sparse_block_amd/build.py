@@ -3,7 +3,8 @@
     python -m long_context_sparse_block_amd.build [--verbose]
 
 Every source under csrc/ is compiled with hipcc for gfx950 (one object per
-file, in parallel) and linked into one shared library next to this file.
+file, in parallel) and linked into one shared library next to this file
+(with zlib, which the host-side literal-flag function uses).
 """
 
 import concurrent.futures
@@ -19,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIBDIR = os.path.join(HERE, "lib")
 LIBNAME = "libsparse_attn.so"
-SOURCES = ["host_common.hip", "mask_build.hip", "bsa_fwd.hip", "offset_fwd.hip"]
+SOURCES = ["host_common.hip", "mask_build.hip", "bsa_fwd.hip", "offset_fwd.hip", "literal_flags.cpp"]
 ARCH = "gfx950"
 
 
@@ -68,7 +69,7 @@ def build(verbose=False, jobs=None):
         list(ex.map(lambda c: _run(c, verbose), cmds))
     lib = os.path.join(LIBDIR, LIBNAME)
     tmp = lib + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lz"], verbose)
     os.replace(tmp, lib)
     return lib
 

@@ -7,9 +7,11 @@ nothing else from this package.
 
 Inputs: Q, K, V iid N(0, 1), drawn as float32 from ``torch.Generator`` seeded
 per workload (q, then k, then v), then rounded to the compute dtype with
-round-to-nearest-even.
+round-to-nearest-even.  Byte streams for gzip-derived literal flags come from
+``synthetic_bytes`` (seeded numpy generator; it stands in for book text).
 """
 
+import numpy as np
 import torch
 
 BF16 = "bf16"
@@ -34,6 +36,14 @@ BLOCK_WORKLOADS = {
         win_before=1, win_after=1, win_clamp=True, global_blocks=[0, 63],
         num_random=3, literal_mode="none", literal_p=0.0, mask_seed=3,
         groups="shared", qkv_seed=1003),
+    # Sec. 4.1 of the compression paper: 8192-byte sequences, 128-byte
+    # blocks, literal flags from per-block gzip sizes, +-1-block local window,
+    # no globals (the "Gzip-Guided" mask); 12 heads of d = 64.
+    "gzip-guided": dict(
+        B=4, H=12, N=8192, d=64, block=128, dtype=BF16, causal=True,
+        win_before=1, win_after=0, win_clamp=False, global_blocks=[],
+        num_random=0, literal_mode="pair", literal_p=0.0, mask_seed=7,
+        groups="per-sequence", qkv_seed=1007, literal_source="gzip", text_seed=7),
     "long-context": dict(
         B=1, H=16, N=65536, d=128, block=128, dtype=BF16, causal=True,
         win_before=2, win_after=0, win_clamp=False, global_blocks=[0, 1, 2, 3],
@@ -101,4 +111,45 @@ def random_draws(G, nb, r, causal, seed):
                 continue
             perm = torch.randperm(n, generator=g)[:r]
             out[gi, i, :perm.numel()] = perm.to(torch.int32)
+    return out
+
+
+# Regimes of synthetic byte blocks: highly repetitive, prose-like, dense.
+_REGIMES = ("repetitive", "prose", "dense")
+
+
+def synthetic_bytes(G, n_bytes, block_bytes, seed):
+    """Byte streams [G, n_bytes] (uint8) with block-level variation in redundancy.
+
+    Stand-in for book text: each block is written in one regime -- a short
+    phrase repeated (repetitive), words drawn with Zipf-like frequencies from a
+    fixed vocabulary (prose), or uniform printable characters (dense).  The
+    regime persists from block to block with probability 0.6, so literal
+    blocks come in runs as in real text.  Deterministic in ``seed``.
+    """
+    rng = np.random.default_rng(seed)
+    letters = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz", dtype=np.uint8)
+    vocab = [bytes(rng.choice(letters, size=int(rng.integers(2, 10)))) for _ in range(300)]
+    zipf = 1.0 / np.arange(1, len(vocab) + 1)
+    zipf /= zipf.sum()
+    out = np.zeros((G, n_bytes), dtype=np.uint8)
+    nb = n_bytes // block_bytes
+    for g in range(G):
+        regime = int(rng.integers(0, 3))
+        for i in range(nb):
+            if i > 0 and rng.random() >= 0.6:
+                regime = int(rng.integers(0, 3))
+            kind = _REGIMES[regime]
+            if kind == "repetitive":
+                phrase = b" ".join(vocab[int(j)] for j in rng.integers(0, 20, size=int(rng.integers(1, 3)))) + b". "
+                blk = (phrase * (block_bytes // len(phrase) + 1))[:block_bytes]
+            elif kind == "prose":
+                blk = b""
+                while len(blk) < block_bytes:
+                    blk += vocab[int(rng.choice(len(vocab), p=zipf))] + b" "
+                blk = blk[:block_bytes]
+            else:
+                blk = bytes(rng.integers(32, 127, size=block_bytes, dtype=np.uint8))
+            out[g, i * block_bytes:(i + 1) * block_bytes] = np.frombuffer(blk, dtype=np.uint8)
+        out[g, nb * block_bytes:] = 32
     return out

@@ -12,8 +12,8 @@ section / equation / algorithm:
 * "Parameter-free Adaptive Sparse Attention via Compression-Based Content
   Selection" (arXiv 2607.21752) -- block mask M = M^lit U M^local U I (Sec. 3.2,
   Eq. 3; Appendix B, Algorithm 1), expansion to tokens and causal AND (Sec. 3.4
-  "Block-to-token expansion"; Algorithm 1 step 4), literal flags (Sec. 3.1,
-  Eq. 2).
+  "Block-to-token expansion"; Algorithm 1 step 4), literal flags from per-block
+  gzip sizes and the mean threshold (Sec. 3.1, Eq. 1-2; Algorithm 1 steps 1-2).
 * "BigBird" (llm-arch-kb) -- window / global / random graphs and their edge
   counts (Sec. 2 "Derivation"), and the dense-masked formulation (Sec. 3
   "Reference implementation").
@@ -23,10 +23,11 @@ section / equation / algorithm:
 
 Modules:
   rng         SplitMix64 and the counter-keyed draws built on it
+  literal     literal flags from byte content (gzip block sizes, mean threshold)
   block_mask  mask components, union, CSR, longest-first schedule
   attention   block-sparse attention: CSR-gather form and dense-masked form
   offsets     offset table and token-level offset attention
   tiny        pure-Python loop versions for tiny inputs (brute force)
 """
 
-from . import rng, block_mask, attention, offsets, tiny  # noqa: F401
+from . import rng, literal, block_mask, attention, offsets, tiny  # noqa: F401

@@ -16,6 +16,22 @@ BF16_LSE = 2e-3
 F32_TOL = 1e-5
 
 
+def workload_spec(w, **over):
+    """Mask spec of a workload dict.  For gzip-sourced workloads the literal
+    flags come from the library's host implementation (the product path), and
+    they must equal the oracle's flags for the same bytes, bit for bit."""
+    from long_context_sparse_block_amd import api
+    from long_context_sparse_block_amd import workloads as wl
+    from oracle import literal
+    if w.get("literal_source") == "gzip" and "literal_flags" not in over:
+        data = wl.synthetic_bytes(w["B"], w["N"], w["block"], w["text_seed"])
+        flags, _ = api.sparse_attn_literal_flags(data, w["block"])
+        ref = literal.literal_flags_batch(data, w["block"])
+        assert np.array_equal(flags, ref), "gzip literal flags differ from the oracle"
+        over = dict(over, literal_flags=flags)
+    return wl.mask_spec(w, **over)
+
+
 def require_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")

@@ -13,7 +13,7 @@ from long_context_sparse_block_amd import api
 from long_context_sparse_block_amd import workloads as wl
 from oracle import attention as oa
 from oracle import block_mask as bm
-from tests.gpu_util import announce, compare, f64, require_gpu
+from tests.gpu_util import announce, compare, f64, require_gpu, workload_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -50,12 +50,12 @@ def test_tiny_fp32_full_parity():
     _run(w, wl.mask_spec(w))
 
 
-@pytest.mark.parametrize("name,B,H", [("compression-guided", 4, 2), ("bigbird", 2, 3)])
+@pytest.mark.parametrize("name,B,H", [("compression-guided", 4, 2), ("bigbird", 2, 3), ("gzip-guided", 4, 2)])
 def test_bf16_reduced_heads_full_parity(name, B, H):
     require_gpu()
     w = dict(wl.BLOCK_WORKLOADS[name], name=name)
     announce(f"[bsa] {name} reduced B={B} H={H} N={w['N']}")
-    _run(w, wl.mask_spec(dict(w, B=B, H=H)), B=B, H=H)
+    _run(w, workload_spec(dict(w, B=B, H=H)), B=B, H=H)
 
 
 def test_long_context_reduced_length_full_parity():
@@ -73,13 +73,13 @@ def _samples(B, H, N, block, n, seed):
     return sorted(out)
 
 
-@pytest.mark.parametrize("name", ["compression-guided", "bigbird", "long-context"])
+@pytest.mark.parametrize("name", ["compression-guided", "bigbird", "gzip-guided", "long-context"])
 def test_full_size_sampled_rows(name):
     require_gpu()
     w = dict(wl.BLOCK_WORKLOADS[name], name=name)
     announce(f"[bsa] {name} full size {w['B']}x{w['H']}x{w['N']}x{w['d']} sampled")
     samples = _samples(w["B"], w["H"], w["N"], w["block"], 96, 7)
-    _run(w, wl.mask_spec(w), samples=samples)
+    _run(w, workload_spec(w), samples=samples)
 
 
 @pytest.mark.parametrize("name", ["compression-guided"])

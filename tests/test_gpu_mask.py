@@ -10,7 +10,7 @@ import torch
 from long_context_sparse_block_amd import api
 from long_context_sparse_block_amd import workloads as wl
 from oracle import block_mask as bm
-from tests.gpu_util import announce, require_gpu
+from tests.gpu_util import announce, require_gpu, workload_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _check_csr(spec, what):
 @pytest.mark.parametrize("name", list(wl.BLOCK_WORKLOADS))
 def test_workload_masks_bitexact(name):
     require_gpu()
-    spec = wl.mask_spec(wl.BLOCK_WORKLOADS[name])
+    spec = workload_spec(wl.BLOCK_WORKLOADS[name])
     nnz = _check_csr(spec, name)
     assert nnz > 0
 
