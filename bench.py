@@ -9,8 +9,9 @@ attention forward.  Inputs are resident in HBM before timing starts.  The value
 is algorithmic TFLOP/s: 4 * d * (unmasked query/key pairs) per step / step time
 (the diagonal block counts b(b+1)/2 pairs; blocks after the query block none).
 
-Prints ONE JSON line.  Secondary workloads (BigBird, gzip-guided, long-context,
-Fibonacci offsets) are measured in the same run and reported under "secondary".
+Prints ONE JSON line.  Secondary workloads (BigBird, gzip-guided with and
+without head groups, long-context, Fibonacci offsets) are measured in the same
+run and reported under "secondary".
 The gzip-guided line takes its literal flags from per-block gzip sizes of
 synthetic byte streams, computed on the host by the library; their host time is
 reported beside the device step (mask build + forward), which it is not part of.
@@ -124,6 +125,8 @@ def block_workload(name, steps, warmup, kernel_iters):
         spec = wl.mask_spec(w, literal_flags=flags)
     else:
         spec = wl.mask_spec(w)
+    if w.get("head_groups"):
+        spec = api.head_group_spec(spec, w["H"])
     dt = wl.torch_dtype(w["dtype"])
     q, k, v = [t.cuda() for t in wl.make_qkv(w["B"], w["H"], w["N"], w["d"], dt, w["qkv_seed"])]
     plan = api.BlockSparsePlan(spec, q, k, v)
@@ -267,7 +270,8 @@ def main():
     }
     if not args.no_secondary:
         sec = []
-        for name, iters in (("bigbird", 200), ("gzip-guided", 200), ("long-context", 20)):
+        for name, iters in (("bigbird", 200), ("gzip-guided", 200), ("gzip-head-groups", 200),
+                            ("long-context", 20)):
             r = block_workload(name, steps=iters, warmup=3, kernel_iters=iters)
             ach = r["flops"] / (r["fwd_ms"] * 1e-3) / 1e12
             line = {"workload": name, "value": round(r["flops"] / (r["step_ms"] * 1e-3) / 1e12, 3),

@@ -97,12 +97,32 @@ enum {
  * ((key >> 32) * n) >> 32, repeats skipped, stop at min(r, n) values or 64 r
  * candidates.
  *
- * Literal flags: `literal_flags` (DEVICE uint8 [G][num_blocks], nonzero =
- * literal) gives them explicitly; if NULL, block j of group g is literal iff
- * (key(seed, 1, g, j, 0) >> 32) < floor(literal_p * 2^32).
+ * Literal flags: `literal_flags` (DEVICE uint8 [F][num_blocks], nonzero =
+ * literal; F = G, or ceil(G / P) with a group period P) gives them explicitly;
+ * if NULL, block j of flag group f is literal iff
+ * (key(seed, 1, f, j, 0) >> 32) < floor(literal_p * 2^32).  Group g reads flag
+ * group f = g (f = g / P with a period).
  * key(seed, t, a, b, c) = sm(sm(sm(sm(sm(seed) ^ t) ^ a) ^ b) ^ c) with sm the
  * SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).
  */
+/* Components of the union that a mask may leave out (sa_mask_desc.exclude_parts,
+ * and per group through group_period / period_exclude).  The identity is always
+ * kept.  The compression paper's head groups (Sec. 3.3) are: local heads =
+ * window U I (exclude SA_PART_LITERAL), long-range heads = literal U I (exclude
+ * SA_PART_WINDOW; the literal component still skips the window band
+ * |i - j| <= w), hybrid heads = the full mask.  With one mask group per
+ * (sequence, head), g = b * H + h, group_period = H and period_exclude[h] = the
+ * head's exclusions, every head of a sequence shares that sequence's literal
+ * flags (row b) and sparse_attn_fwd takes mask_batch_stride = H,
+ * mask_head_stride = 1. */
+#define SA_MAX_PERIOD 64
+enum {
+  SA_PART_WINDOW = 1,
+  SA_PART_GLOBAL = 2,
+  SA_PART_RANDOM = 4,
+  SA_PART_LITERAL = 8,
+};
+
 typedef struct sa_mask_desc {
   int32_t num_blocks;           /* N_b = N / block, 1..SA_MAX_BLOCKS              */
   int32_t num_groups;           /* G >= 1 independent masks                        */
@@ -118,6 +138,11 @@ typedef struct sa_mask_desc {
   const uint8_t* literal_flags; /* DEVICE [G][N_b] or NULL                         */
   double literal_p;             /* in [0, 1]; used when literal_flags is NULL      */
   uint64_t seed;
+  int32_t exclude_parts;        /* SA_PART_* bits left out of every group's union  */
+  int32_t group_period;         /* P, 0..SA_MAX_PERIOD; 0 = no per-group pattern    */
+  int32_t period_exclude[SA_MAX_PERIOD]; /* when P > 0: group g also leaves out
+                                   period_exclude[g % P], and reads its literal
+                                   flags (explicit or drawn) as group g / P     */
 } sa_mask_desc;
 
 /* Upper bound on the number of CSR entries the mask can have:

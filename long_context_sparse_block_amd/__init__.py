@@ -9,6 +9,8 @@ from .api import (  # noqa: F401
     BlockMask,
     SparseAttnError,
     fibonacci_base,
+    head_group_spec,
+    mask_preset,
     offset_attn_fwd,
     offset_attn_make_table,
     sparse_attn_build_mask,

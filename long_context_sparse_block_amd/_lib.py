@@ -25,10 +25,16 @@ SA_LIT_NONE = 0
 SA_LIT_PAIR = 1
 SA_LIT_ANYQ = 2
 
+SA_PART_WINDOW = 1
+SA_PART_GLOBAL = 2
+SA_PART_RANDOM = 4
+SA_PART_LITERAL = 8
+
 SA_MAX_GLOBAL = 64
 SA_MAX_RANDOM = 32
 SA_MAX_BLOCKS = 16384
 SA_MAX_OFFSETS = 128
+SA_MAX_PERIOD = 64
 
 # every function the header declares, with (restype, argtypes)
 _i32, _i64, _f32, _f64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint64
@@ -51,6 +57,9 @@ class MaskDesc(ctypes.Structure):
         ("literal_flags", _p),
         ("literal_p", _f64),
         ("seed", _u64),
+        ("exclude_parts", _i32),
+        ("group_period", _i32),
+        ("period_exclude", _i32 * 64),
     ]
 
 

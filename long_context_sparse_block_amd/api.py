@@ -77,7 +77,72 @@ def _mask_desc(spec, device, keep):
         d.literal_flags = t.data_ptr()
     d.literal_p = float(spec.get("literal_p") or 0.0)
     d.seed = int(spec.get("seed") or 0) & ((1 << 64) - 1)
+    d.exclude_parts = _parts(spec.get("exclude_parts"))
+    pe = spec.get("period_exclude") or []
+    if len(pe) > L.SA_MAX_PERIOD:
+        raise ValueError("period_exclude longer than SA_MAX_PERIOD")
+    d.group_period = len(pe)
+    for n, parts in enumerate(pe):
+        d.period_exclude[n] = _parts(parts)
     return d
+
+
+_PARTS = {"window": L.SA_PART_WINDOW, "global": L.SA_PART_GLOBAL, "random": L.SA_PART_RANDOM,
+          "literal": L.SA_PART_LITERAL}
+
+
+def _parts(names):
+    """SA_PART_* bits of a list of component names (or an int)."""
+    if names is None:
+        return 0
+    if isinstance(names, int):
+        return names
+    bits = 0
+    for n in names:
+        bits |= _PARTS[n]
+    return bits
+
+
+def mask_preset(name, num_blocks, num_groups=1, causal=True, **over):
+    """Mask spec of an attention variant the compression paper compares (Sec. 4.2).
+
+    "dense" (every earlier block), "local-only" (+-1-block window),
+    "longformer" (+-4-block window, a global block every 8 blocks),
+    "literal-pure" (literal-to-literal pairs and the identity, no window: the
+    band |i - j| <= w of M^lit is then empty), "gzip-guided" (literal pairs and
+    a +-1-block window).  Literal flags go in ``literal_flags`` (e.g. from
+    sparse_attn_literal_flags) or are drawn with ``literal_p``.
+    """
+    w = {"dense": num_blocks, "local-only": 1, "longformer": 4, "literal-pure": 0, "gzip-guided": 1}
+    if name not in w:
+        raise ValueError(f"unknown preset {name!r}")
+    spec = dict(num_blocks=num_blocks, num_groups=num_groups, causal=causal, win_before=w[name],
+                win_after=0 if causal else w[name], win_clamp=False, global_blocks=[], num_random=0,
+                random_blocks=None, literal_mode="none", literal_flags=None, literal_p=0.0, seed=0)
+    if name == "longformer":
+        spec["global_blocks"] = list(range(0, num_blocks, 8))
+    if name in ("literal-pure", "gzip-guided"):
+        spec["literal_mode"] = "pair"
+    spec.update(over)
+    return spec
+
+
+def head_group_spec(spec, H, local=0.5, long_range=0.25):
+    """Per-head masks of the compression paper's head groups (Sec. 3.3).
+
+    Heads [0, L) are local (window U I), [L, L + R) long-range (literal U I),
+    the rest hybrid (the full mask), with L = floor(local H), R = floor(long_range
+    H) (12 heads: 6, 3, 3).  The result has one mask group per (group of
+    ``spec``, head): G' = G H, group g = g0 H + h, and every head of a group
+    shares its literal flags.  Pass its mask_batch_stride / mask_head_stride to
+    sparse_attn_fwd.
+    """
+    L_, R_ = int(local * H), int(long_range * H)
+    pe = [["literal"]] * L_ + [["window"]] * R_ + [[]] * (H - L_ - R_)
+    out = dict(spec, num_groups=spec["num_groups"] * H, period_exclude=pe)
+    out["mask_batch_stride"] = int(spec.get("mask_batch_stride") or 0) * H
+    out["mask_head_stride"] = 1
+    return out
 
 
 def sparse_attn_mask_capacity(spec):

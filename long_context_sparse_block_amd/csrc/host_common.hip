@@ -63,7 +63,7 @@ const char* sa_last_hip_error(void) { return g_last_error; }
 int32_t sa_version(void) { return 1; }
 
 int32_t sa_mask_desc_layout(int64_t* out, int32_t n) {
-  const int64_t v[15] = {(int64_t)sizeof(sa_mask_desc),
+  const int64_t v[18] = {(int64_t)sizeof(sa_mask_desc),
                          (int64_t)offsetof(sa_mask_desc, num_blocks),
                          (int64_t)offsetof(sa_mask_desc, num_groups),
                          (int64_t)offsetof(sa_mask_desc, causal),
@@ -77,10 +77,13 @@ int32_t sa_mask_desc_layout(int64_t* out, int32_t n) {
                          (int64_t)offsetof(sa_mask_desc, literal_mode),
                          (int64_t)offsetof(sa_mask_desc, literal_flags),
                          (int64_t)offsetof(sa_mask_desc, literal_p),
-                         (int64_t)offsetof(sa_mask_desc, seed)};
-  if (out == nullptr) return 15;
-  for (int32_t i = 0; i < n && i < 15; ++i) out[i] = v[i];
-  return 15;
+                         (int64_t)offsetof(sa_mask_desc, seed),
+                         (int64_t)offsetof(sa_mask_desc, exclude_parts),
+                         (int64_t)offsetof(sa_mask_desc, group_period),
+                         (int64_t)offsetof(sa_mask_desc, period_exclude)};
+  if (out == nullptr) return 18;
+  for (int32_t i = 0; i < n && i < 18; ++i) out[i] = v[i];
+  return 18;
 }
 
 }  // extern "C"

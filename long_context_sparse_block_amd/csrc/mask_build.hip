@@ -20,6 +20,9 @@ constexpr int kScanThreads = 1024;
 struct MaskArgs {
   int32_t nb, G, causal, wb, wa, clamp;
   int32_t num_global, num_random, lit_mode;
+  int32_t excl;  // SA_PART_* bits left out of every group's union
+  int32_t period;  // P > 0: per-group exclusions period_excl[g % P], flags row g / P
+  int32_t period_excl[SA_MAX_PERIOD];
   int32_t globals[SA_MAX_GLOBAL];
   const int32_t* random_blocks;
   const uint8_t* lit_flags;
@@ -34,6 +37,8 @@ struct MaskArgs {
 // Everything a wave needs to decide membership for one row.
 struct RowCtx {
   int32_t g, i;
+  int32_t fg;    // literal-flag group (g, or g / P)
+  int32_t excl;  // components left out of this group's union
   bool valid;
   bool row_global;
   bool lit_i;
@@ -42,7 +47,7 @@ struct RowCtx {
 };
 
 __device__ __forceinline__ bool literal_of(const MaskArgs& a, const RowCtx& c, int32_t j) {
-  if (a.lit_flags) return a.lit_flags[(int64_t)c.g * a.nb + j] != 0;
+  if (a.lit_flags) return a.lit_flags[(int64_t)c.fg * a.nb + j] != 0;
   const uint64_t h = sa::splitmix64(sa::splitmix64(c.lit_key ^ (uint64_t)j) ^ 0ull);
   return (h >> 32) < a.lit_thr;
 }
@@ -61,8 +66,10 @@ __device__ RowCtx setup_row(const MaskArgs& a, int64_t r, int32_t* draws, int la
   c.valid = r < R;
   c.g = c.valid ? (int32_t)(r / a.nb) : 0;
   c.i = c.valid ? (int32_t)(r - (int64_t)c.g * a.nb) : 0;
+  c.fg = a.period > 0 ? c.g / a.period : c.g;
+  c.excl = a.excl | (a.period > 0 ? a.period_excl[c.g % a.period] : 0);
   c.row_global = is_global(a, c.i);
-  c.lit_key = sa::splitmix64(sa::splitmix64(sa::splitmix64(a.seed) ^ 1ull) ^ (uint64_t)c.g);
+  c.lit_key = sa::splitmix64(sa::splitmix64(sa::splitmix64(a.seed) ^ 1ull) ^ (uint64_t)c.fg);
   c.lit_i = (a.lit_mode != SA_LIT_NONE) && c.valid && literal_of(a, c, c.i);
   c.ndraw = 0;
   if (lane == 0 && c.valid && a.num_random > 0) {
@@ -102,23 +109,26 @@ __device__ __forceinline__ bool member(const MaskArgs& a, const RowCtx& c, const
   if (a.causal && j > i) return false;
   if (j == i) return true;
   // local window
-  if (a.causal) {
-    if (j >= i - a.wb) return true;
-  } else if (a.clamp) {
-    const int32_t width = a.wb + a.wa + 1;
-    if (width >= a.nb) return true;
-    const int32_t start = min(max(i - a.wb, 0), a.nb - width);
-    if (j >= start && j < start + width) return true;
-  } else if (j >= i - a.wb && j <= i + a.wa) {
-    return true;
+  if (!(c.excl & SA_PART_WINDOW)) {
+    if (a.causal) {
+      if (j >= i - a.wb) return true;
+    } else if (a.clamp) {
+      const int32_t width = a.wb + a.wa + 1;
+      if (width >= a.nb) return true;
+      const int32_t start = min(max(i - a.wb, 0), a.nb - width);
+      if (j >= start && j < start + width) return true;
+    } else if (j >= i - a.wb && j <= i + a.wa) {
+      return true;
+    }
   }
   // global rows / columns
-  if (c.row_global || is_global(a, j)) return true;
+  if (!(c.excl & SA_PART_GLOBAL) && (c.row_global || is_global(a, j))) return true;
   // random draws
-  for (int m = 0; m < c.ndraw; ++m)
-    if (draws[m] == j) return true;
+  if (!(c.excl & SA_PART_RANDOM))
+    for (int m = 0; m < c.ndraw; ++m)
+      if (draws[m] == j) return true;
   // literal blocks outside the window band
-  if (a.lit_mode != SA_LIT_NONE && (j < i - a.wb || j > i + a.wa)) {
+  if (!(c.excl & SA_PART_LITERAL) && a.lit_mode != SA_LIT_NONE && (j < i - a.wb || j > i + a.wa)) {
     if (a.lit_mode == SA_LIT_PAIR && !c.lit_i) return false;
     return literal_of(a, c, j);
   }
@@ -218,6 +228,10 @@ sa_status check_desc(const sa_mask_desc* d) {
   }
   if (d->num_random < 0 || d->num_random > SA_MAX_RANDOM) return SA_ERR_INVALID;
   if (d->literal_mode < SA_LIT_NONE || d->literal_mode > SA_LIT_ANYQ) return SA_ERR_INVALID;
+  if (d->exclude_parts < 0 || d->exclude_parts > 15) return SA_ERR_INVALID;
+  if (d->group_period < 0 || d->group_period > SA_MAX_PERIOD) return SA_ERR_INVALID;
+  for (int n = 0; n < d->group_period; ++n)
+    if (d->period_exclude[n] < 0 || d->period_exclude[n] > 15) return SA_ERR_INVALID;
   if (d->literal_mode != SA_LIT_NONE && d->literal_flags == nullptr &&
       !(d->literal_p >= 0.0 && d->literal_p <= 1.0))
     return SA_ERR_INVALID;
@@ -262,6 +276,9 @@ sa_status sparse_attn_build_mask(const sa_mask_desc* d, int32_t* row_ptr, int32_
   a.random_blocks = d->random_blocks;
   a.lit_mode = d->literal_mode;
   a.lit_flags = d->literal_flags;
+  a.excl = d->exclude_parts;
+  a.period = d->group_period;
+  for (int n = 0; n < d->group_period; ++n) a.period_excl[n] = d->period_exclude[n];
   {
     // floor(p * 2^32) in double, clamped to [0, 2^32]
     const double t = floor(d->literal_p * 4294967296.0);

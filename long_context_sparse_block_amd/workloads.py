@@ -44,6 +44,14 @@ BLOCK_WORKLOADS = {
         win_before=1, win_after=0, win_clamp=False, global_blocks=[],
         num_random=0, literal_mode="pair", literal_p=0.0, mask_seed=7,
         groups="per-sequence", qkv_seed=1007, literal_source="gzip", text_seed=7),
+    # the same with the paper's head groups (Sec. 3.3): heads 0-5 local,
+    # 6-8 long-range, 9-11 hybrid; one mask group per (sequence, head)
+    "gzip-head-groups": dict(
+        B=4, H=12, N=8192, d=64, block=128, dtype=BF16, causal=True,
+        win_before=1, win_after=0, win_clamp=False, global_blocks=[],
+        num_random=0, literal_mode="pair", literal_p=0.0, mask_seed=7,
+        groups="per-sequence", qkv_seed=1008, literal_source="gzip", text_seed=7,
+        head_groups=True),
     "long-context": dict(
         B=1, H=16, N=65536, d=128, block=128, dtype=BF16, causal=True,
         win_before=2, win_after=0, win_clamp=False, global_blocks=[0, 1, 2, 3],

@@ -16,6 +16,10 @@ A mask spec is a plain dict with the keys
   literal_flags   optional explicit flags, uint8 array [G, N_b]
   literal_p    Bernoulli rate used when literal_flags is None
   seed         key of every draw
+  exclude_parts   optional list of component names left out of the union
+               ("window", "global", "random", "literal"); the identity stays
+  period_exclude  optional list of P such lists: group g also leaves out
+               period_exclude[g % P] and reads literal flags of group g // P
 
 Each component is built as a dense N_b x N_b boolean matrix per group, the way
 the pages write them, and the mask is their union (Eq. 3 of "Parameter-free
@@ -35,24 +39,38 @@ def _get(spec, key, default):
     return default if v is None else v
 
 
+def period(spec):
+    """P: with P > 0, group g has the extra exclusions period_exclude[g % P] and
+    the literal flags of flag group g // P (e.g. one group per (sequence, head)
+    with P = H: every head of a sequence shares that sequence's flags)."""
+    return len(_get(spec, "period_exclude", []))
+
+
+def flag_group(spec, g):
+    P = period(spec)
+    return g // P if P else g
+
+
 def literal_flags(spec):
-    """uint8 [G, N_b] literal flags: the explicit ones, else Bernoulli draws.
+    """uint8 [F, N_b] literal flags per flag group (F = G, or ceil(G / P) with a
+    period): the explicit ones, else Bernoulli draws.
 
     Compression paper, Sec. 3.1 Eq. 2 defines l_i = 1[r_i > mean r] from gzip
-    ratios; the synthetic workloads replace the ratios with seeded Bernoulli(p)
-    flags (rng.literal_flag).
+    ratios (see ``literal``); the synthetic workloads may replace the ratios
+    with seeded Bernoulli(p) flags (rng.literal_flag).
     """
     G, nb = spec["num_groups"], spec["num_blocks"]
+    F = flag_group(spec, G - 1) + 1
     explicit = spec.get("literal_flags")
     if explicit is not None:
-        f = np.asarray(explicit, dtype=np.uint8).reshape(G, nb)
+        f = np.asarray(explicit, dtype=np.uint8).reshape(-1, nb)[:F]
         return (f != 0).astype(np.uint8)
     p = float(_get(spec, "literal_p", 0.0))
     seed = int(_get(spec, "seed", 0))
-    out = np.zeros((G, nb), dtype=np.uint8)
-    for g in range(G):
+    out = np.zeros((F, nb), dtype=np.uint8)
+    for f in range(F):
         for j in range(nb):
-            out[g, j] = rng.literal_flag(seed, g, j, p)
+            out[f, j] = rng.literal_flag(seed, f, j, p)
     return out
 
 
@@ -169,7 +187,7 @@ def components(spec, g, flags=None):
         "window": window_component(nb, causal, wb, wa, clamp),
         "global": global_component(nb, causal, _get(spec, "global_blocks", [])),
         "random": random_component(spec, g),
-        "literal": literal_component(nb, causal, wb, wa, flags[g], mode),
+        "literal": literal_component(nb, causal, wb, wa, flags[flag_group(spec, g)], mode),
     }
 
 
@@ -181,12 +199,18 @@ def block_mask(spec):
     """
     G, nb = spec["num_groups"], spec["num_blocks"]
     flags = literal_flags(spec)
+    # components a head group leaves out (compression paper, Sec. 3.3: local
+    # heads use M^local U I, long-range heads M^lit U I); I is always kept
+    excluded_all = set(_get(spec, "exclude_parts", None) or [])
+    pe, P = _get(spec, "period_exclude", []), period(spec)
     out = np.zeros((G, nb, nb), dtype=bool)
     for g in range(G):
+        excluded = excluded_all | (set(pe[g % P]) if P else set())
         comp = components(spec, g, flags)
         m = np.zeros((nb, nb), dtype=bool)
-        for c in comp.values():
-            m |= c
+        for name, c in comp.items():
+            if name not in excluded:
+                m |= c
         if spec["causal"]:
             m &= np.tril(np.ones((nb, nb), dtype=bool))
         out[g] = m

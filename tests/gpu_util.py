@@ -29,7 +29,10 @@ def workload_spec(w, **over):
         ref = literal.literal_flags_batch(data, w["block"])
         assert np.array_equal(flags, ref), "gzip literal flags differ from the oracle"
         over = dict(over, literal_flags=flags)
-    return wl.mask_spec(w, **over)
+    spec = wl.mask_spec(w, **over)
+    if w.get("head_groups"):
+        spec = api.head_group_spec(spec, w["H"])
+    return spec
 
 
 def require_gpu():

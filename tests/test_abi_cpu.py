@@ -39,9 +39,11 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 
 def test_mask_desc_layout_matches_binding(lib):
-    out = (ctypes.c_int64 * 15)()
-    assert lib.sa_mask_desc_layout(out, 15) == 15
     fields = [f[0] for f in L.MaskDesc._fields_]
+    n = lib.sa_mask_desc_layout(None, 0)
+    assert n == len(fields) + 1
+    out = (ctypes.c_int64 * n)()
+    assert lib.sa_mask_desc_layout(out, n) == n
     assert out[0] == ctypes.sizeof(L.MaskDesc)
     for n, name in enumerate(fields):
         assert out[n + 1] == getattr(L.MaskDesc, name).offset, name

@@ -50,7 +50,8 @@ def test_tiny_fp32_full_parity():
     _run(w, wl.mask_spec(w))
 
 
-@pytest.mark.parametrize("name,B,H", [("compression-guided", 4, 2), ("bigbird", 2, 3), ("gzip-guided", 4, 2)])
+@pytest.mark.parametrize("name,B,H", [("compression-guided", 4, 2), ("bigbird", 2, 3), ("gzip-guided", 4, 2),
+                                      ("gzip-head-groups", 2, 12)])
 def test_bf16_reduced_heads_full_parity(name, B, H):
     require_gpu()
     w = dict(wl.BLOCK_WORKLOADS[name], name=name)
@@ -73,7 +74,8 @@ def _samples(B, H, N, block, n, seed):
     return sorted(out)
 
 
-@pytest.mark.parametrize("name", ["compression-guided", "bigbird", "gzip-guided", "long-context"])
+@pytest.mark.parametrize("name", ["compression-guided", "bigbird", "gzip-guided", "gzip-head-groups",
+                                  "long-context"])
 def test_full_size_sampled_rows(name):
     require_gpu()
     w = dict(wl.BLOCK_WORKLOADS[name], name=name)

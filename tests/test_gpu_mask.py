@@ -82,3 +82,33 @@ def _fuzz_spec(seed):
 def test_fuzz_masks_bitexact(seed):
     require_gpu()
     _check_csr(_fuzz_spec(seed), f"fuzz {seed}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_presets_and_head_groups_bitexact(causal):
+    require_gpu()
+    G, nb = 3, 64
+    flags = wl.random_flags(G, nb, 0.45, 21).numpy()
+    for name in ("dense", "local-only", "longformer", "literal-pure", "gzip-guided"):
+        spec = api.mask_preset(name, nb, G, causal, literal_flags=flags,
+                               mask_batch_stride=1, mask_head_stride=0)
+        _check_csr(spec, f"preset {name} causal={causal}")
+    base = api.mask_preset("gzip-guided", nb, G, causal, literal_flags=flags,
+                           mask_batch_stride=1, mask_head_stride=0)
+    _check_csr(api.head_group_spec(base, 12), f"head groups causal={causal}")
+    # drawn flags with a period: every head of a sequence draws the same flags
+    drawn = dict(base, literal_flags=None, literal_p=0.3, seed=77)
+    _check_csr(api.head_group_spec(drawn, 8), f"head groups drawn causal={causal}")
+    # a period with every component on, and exclusions of globals / randoms
+    bb = dict(base, global_blocks=[0, 31], num_random=2, period_exclude=[["global"], ["random"], []],
+              num_groups=3 * G)
+    _check_csr(bb, f"period over globals/randoms causal={causal}")
+
+
+def test_exclusion_and_period_errors():
+    require_gpu()
+    base = api.mask_preset("local-only", 16)
+    with pytest.raises(api.SparseAttnError):
+        api.sparse_attn_build_mask(dict(base, exclude_parts=99))
+    with pytest.raises((api.SparseAttnError, ValueError)):
+        api.sparse_attn_build_mask(dict(base, period_exclude=[[]] * 65))
