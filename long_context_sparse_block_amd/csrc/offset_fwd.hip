@@ -3,21 +3,29 @@
 // every distance delta of a table shared by all queries (a dense window
 // {0..W} plus rounded scaled Fibonacci rungs), skipping t - delta < 0.
 //
-// Every (query, key) pair is a single dot product and a single V update, so
-// the work is bound by moving K / V rows, not by matrix throughput.  bf16 path:
-//   * a workgroup owns 64 consecutive queries of one head; four lanes share a
-//     query, each holding a quarter of the head dimension, so the rows read for
-//     a fixed distance form contiguous, fully used 64-byte segments and the
-//     dot product needs only two quad (DPP) reductions;
-//   * the near distances (<= 64) all read inside the span [t0 - R, t0 + 64)
-//     (R = the largest near distance), which is staged once in LDS; the far
-//     rungs are read straight from global memory / L2;
-//   * distances are taken 8 at a time: 8 scores, one online-softmax rescale,
-//     then V is accumulated two keys at a time with bf16 dot2 (the two keys'
-//     values for one column are paired with a byte permute), one instruction
-//     per two multiply-adds;
+// bf16 path (one workgroup = 4 waves walks consecutive 64-query tiles of one
+// head; wave w owns queries t0 + 16 w + i, i < 16):
+//   * near distances (<= 64): every key t - delta of the wave's 16 queries
+//     lies in an 80-row band [t0 + 16 w - 64, t0 + 16 w + 16).  The band's
+//     scores S^T = K Q^T and the product O^T += V^T P^T run on
+//     v_mfma_f32_16x16x32_bf16 over the whole band; entries whose distance is
+//     not in the table get weight 0 (a per-lane bit mask).  K / V rows reach
+//     LDS through a ring of three 64-row blocks filled by direct global->LDS
+//     copies, the next tile's block in flight while the current one is used;
+//     each row is copied once per workgroup.
+//   * far rungs (> 64): each row is used by one query of the tile, so it is
+//     gathered straight into registers (no LDS round trip), four rungs at a
+//     time, with an online-softmax rescale per batch.  The lane layout is the
+//     MFMA output layout: lane l holds query l % 16 and the head-dimension
+//     entries d = 32 c + 8 (l / 16) + e (e < 8), i.e. 16-byte chunks 4 c + l/16
+//     of a row; the O^T tiles take their rows in that permuted d order, so the
+//     far contributions accumulate into the same registers.  A rung's dot
+//     product is reduced over the 4 lanes of a query with two lane-row swaps.
+//   * all global loads of the loop are issued as inline asm and waited for
+//     with explicit vmcnt counts, so waiting for a far batch never waits for
+//     the ring copies issued after it.
 //   * workgroups of one head run on one XCD (blockIdx % 8 selects the XCD), so
-//     every re-read of a K / V row by another query tile is served by its L2.
+//     the far-rung re-reads of a K / V row are served by its L2.
 // fp32 path: one thread per query, plain fp32 arithmetic, for exact checks.
 #include <math.h>
 
@@ -32,7 +40,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;
-constexpr int kNearMax = 64;   // distances up to this are served from the staged span
+constexpr int kNearMax = 64;   // distances up to this are served by the MFMA band
 
 // Raise the dynamic-LDS limit of a kernel once (needed above 64 KiB).
 inline sa_status allow_lds(const void* kern, int bytes) {
@@ -51,8 +59,11 @@ struct OffArgs {
   float* lse;
   int64_t qs[3], ks[3], vs[3], os[3];
   int32_t B, H, H_kv, N, noff;
-  int32_t nnear;  // offsets[0 .. nnear) are <= kNearMax and are read from the staged span
-  int32_t span_r; // largest near offset (rows staged before the tile)
+  int32_t nnear;  // offsets[0 .. nnear) are <= kNearMax (bf16 path: MFMA band)
+  int32_t near64; // 64 is a near distance
+  uint64_t near_bits;  // bit x: distance x (< 64) is in the table
+  int32_t tpw;    // 64-query tiles per workgroup (bf16 path)
+  int32_t nchunk; // workgroups per (batch, head)
   float scale_log2;
   int32_t offs[SA_MAX_OFFSETS];
 };
@@ -103,179 +114,293 @@ __device__ __forceinline__ void tile_of(int w, int BH, int tiles, int& bh, int& 
   }
 }
 
-// 16-byte chunk slot inside a staged row (XOR swizzle against bank conflicts
-// between the 16 rows one wave-instruction touches).
-__device__ __forceinline__ int swz_row(int c, int row) { return c ^ (row & 7); }
-
 // (v_a, v_b) bf16 pairs -> (lo halves), (hi halves)
 __device__ __forceinline__ uint32_t pair_lo(uint32_t va, uint32_t vb) { return __builtin_amdgcn_perm(vb, va, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t va, uint32_t vb) { return __builtin_amdgcn_perm(vb, va, 0x07060302u); }
 
-// Sum over the 4 lanes of a quad (DPP quad permutes, no LDS traffic).
-__device__ __forceinline__ float quad_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-  return x;
+// 16-byte chunk slot of chunk c in a staged row: XOR with bits (0, 2, 1) of the
+// row's low three bits, so that the 8 rows of one ds_read_b128 phase hit
+// distinct slots and the 4 rows of one transpose-read phase fall in two
+// different groups of four slots.
+__device__ __forceinline__ int swz(int c, int row) {
+  const int r = row & 7;
+  return c ^ ((r & 1) | ((r & 2) << 1) | ((r & 4) >> 1));
 }
 
 template <int D>
-struct OffCfg {
-  static constexpr int LPQ = 4;                 // lanes per query
-  static constexpr int TQ = 64;                 // queries per workgroup
-  static constexpr int NT = TQ * LPQ;           // threads
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int CPL = CPR / LPQ;         // chunks per lane: c = j + 4 m
-  static constexpr int ROWB = D * 2;
-  static constexpr int SPAN = TQ + kNearMax;    // staged rows
-  static constexpr int LDSB = 2 * SPAN * ROWB;  // K and V
+struct MCfg {
+  static constexpr int NW = 4;               // waves per workgroup
+  static constexpr int TQ = 64;              // queries per tile step (16 per wave)
+  static constexpr int ROWB = 2 * D;         // bytes per K / V row
+  static constexpr int RING = 192;           // staged rows: three 64-row blocks
+  static constexpr int RINGB = RING * ROWB;  // bytes of the K ring (the V ring follows)
+  static constexpr int LDSB = 2 * RINGB;
+  static constexpr int NC = D / 32;          // 16-byte chunks a lane holds per row
+  static constexpr int NDT = D / 16;         // 16-row tiles of O^T
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;    // rows per copy wave-instruction
+  static constexpr int IPW = ROWB / 64;      // copy wave-instructions per wave, block and matrix
+  static constexpr int FC = D == 64 ? 4 : 2; // far rungs per register batch (even)
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void offset_bf16_kernel(OffArgs a) {
-  using C = OffCfg<D>;
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffArgs a) {
+  using C = MCfg<D>;
+  constexpr int NC = C::NC, NDT = C::NDT, FC = C::FC, ROWB = C::ROWB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* ks = smem;
-  uint8_t* vs = smem + C::SPAN * C::ROWB;
+  const uint32_t lds0 = sa::lds_addr(smem);
 
-  const int tid = threadIdx.x;
-  const int ql = tid / C::LPQ, j = tid % C::LPQ;
-  const int tiles = (a.N + C::TQ - 1) / C::TQ;
-  int bh, tile;
-  tile_of(blockIdx.x, a.B * a.H, tiles, bh, tile);
+  const int lane = threadIdx.x & 63, w = sa::uniform(threadIdx.x >> 6);
+  const int i = lane & 15, g = lane >> 4;
+  const int ntiles = (a.N + C::TQ - 1) / C::TQ;
+  int bh, chunk;
+  tile_of(blockIdx.x, a.B * a.H, a.nchunk, bh, chunk);
+  const int ti0 = chunk * a.tpw, ti1 = min(ti0 + a.tpw, ntiles);
   const int b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
-  const int t0 = tile * C::TQ;
-  const int t = t0 + ql;
-  const bool live = t < a.N;
-  const int tq = live ? t : a.N - 1;
 
-  const uint16_t* Q = (const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1];
-  const char* Kb = (const char*)((const uint16_t*)a.k + b * a.ks[0] + kvh * a.ks[1]);
-  const char* Vb = (const char*)((const uint16_t*)a.v + b * a.vs[0] + kvh * a.vs[1]);
-  const uint32_t krow = (uint32_t)a.ks[2] * 2u, vrow = (uint32_t)a.vs[2] * 2u;  // bytes per row
+  const char* Qh = (const char*)((const uint16_t*)a.q + b * a.qs[0] + h * a.qs[1]);
+  const char* Kh = (const char*)((const uint16_t*)a.k + b * a.ks[0] + kvh * a.ks[1]);
+  const char* Vh = (const char*)((const uint16_t*)a.v + b * a.vs[0] + kvh * a.vs[1]);
+  uint16_t* Oh = (uint16_t*)a.o + b * a.os[0] + h * a.os[1];
+  float* Lh = a.lse + ((int64_t)b * a.H + h) * a.N;
+  const uint32_t qrow = (uint32_t)a.qs[2] * 2u, krow = (uint32_t)a.ks[2] * 2u, vrow = (uint32_t)a.vs[2] * 2u;
+  const bool has_near = a.nnear > 0;
+  const int nfar = a.noff - a.nnear;
+  const float c2 = a.scale_log2;
+  const uint32_t lone = g == 0 ? 0x3f803f80u : 0u;  // far weights are counted once per query
 
-  // stage rows [t0 - R, t0 + TQ) of K and V (rows outside [0, N) are skipped;
-  // no query reads them)
-  const int R = a.span_r;
-  const int rows = C::TQ + R;
-  for (int x = tid; x < rows * C::CPR; x += C::NT) {
-    const int lr = x / C::CPR, c = x % C::CPR;
-    const int r = t0 - R + lr;
-    if (r < 0 || r >= a.N) continue;
-    const int off = lr * C::ROWB + swz_row(c, lr) * 16;
-    *(sa::u32x4*)(ks + off) = *(const sa::u32x4*)(Kb + (uint32_t)r * krow + 16u * c);
-    *(sa::u32x4*)(vs + off) = *(const sa::u32x4*)(Vb + (uint32_t)r * vrow + 16u * c);
+  // Band row of this lane's score (block kb, entry r): 16 kb + 4 g + r; its
+  // distance from query i is 64 + i - (16 kb + 4 g + r).  nmask: the distance
+  // is in the table; cmask: the key row is >= 0 in the first tile.
+  uint32_t nmask = 0, cmask = 0;
+#pragma unroll
+  for (int kb = 0; kb < 5; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * kb + 4 * g + r;
+      const int dl = 64 + i - key;
+      const bool in = dl >= 0 && dl <= 64 && (dl < 64 ? ((a.near_bits >> dl) & 1ull) != 0 : a.near64 != 0);
+      nmask |= (uint32_t)in << (4 * kb + r);
+      cmask |= (uint32_t)(key + 16 * w >= 64) << (4 * kb + r);
+    }
+  // LDS offsets inside a 16-row group: K operand (row i, chunk 4u + g) and the
+  // transpose reads of V (row 4g + i/4, the 4 entries of O^T rows 4(i%4).. of
+  // tile dt, i.e. d = 32(dt/2) + 8(i%4) + 4(dt%2) ..).
+  uint32_t kofs[NC], vofs[NDT];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) kofs[u] = i * ROWB + swz(4 * u + g, i) * 16;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int vr = 4 * g + (i >> 2);
+    vofs[dt] = vr * ROWB + swz(4 * (dt >> 1) + (i & 3), vr) * 16 + 8 * (dt & 1);
   }
 
-  // this lane's quarter of q: chunks c = j + 4 m
-  sa::u32x4 qv[C::CPL];
+  // Copy 64-row block blk (>= -1) of K and V into ring slot blk mod 3.  Rows
+  // outside [0, N) are clamped to a valid row: they only meet zero weights.
+  // Every wave issues exactly 2 * IPW copies.
+  auto stage = [&](int blk) {
+    const uint32_t slot = (uint32_t)((blk + 3) % 3);
 #pragma unroll
-  for (int m = 0; m < C::CPL; ++m) qv[m] = *(const sa::u32x4*)(Q + (int64_t)tq * a.qs[2] + 8 * (j + 4 * m));
-  float acc[C::CPL][8];
-#pragma unroll
-  for (int m = 0; m < C::CPL; ++m)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c2 = a.scale_log2;
-  __syncthreads();
-
-  // One chunk of 8 distances [n0, n0 + 8) (entries past n1 repeat the range's
-  // last distance and get weight 0): scores, one rescale, V update.  FAR rows
-  // come from global memory, near ones from the staged span; MASKED: some
-  // query of the tile precedes a distance of the chunk.
-  auto chunk = [&](int n0, int n1, auto far_t, auto masked_t) {
-    constexpr bool FAR = decltype(far_t)::value;
-    constexpr bool MASKED = decltype(masked_t)::value;
-    int src[kChunk];
-    bool ok[kChunk];
-#pragma unroll
-    for (int cc = 0; cc < kChunk; ++cc) {
-      const int delta = a.offs[min(n0 + cc, n1 - 1)];
-      int s0 = tq - delta;
-      ok[cc] = !MASKED || s0 >= 0;
-      if (MASKED) s0 = max(s0, 0);
-      src[cc] = FAR ? s0 : s0 - (t0 - R);  // global row, or row of the span
-    }
-    auto ld = [&](const char* g, const uint8_t* l, uint32_t grow, int cc, int m) -> sa::u32x4 {
-      const int c = j + 4 * m;
-      if (FAR) return *(const sa::u32x4*)(g + (uint32_t)src[cc] * grow + 16u * c);
-      return *(const sa::u32x4*)(l + src[cc] * C::ROWB + swz_row(c, src[cc]) * 16);
-    };
-    float y[kChunk];
-#pragma unroll
-    for (int cc = 0; cc < kChunk; ++cc) {
-      float dot = 0.f;
-#pragma unroll
-      for (int m = 0; m < C::CPL; ++m) {
-        const sa::u32x4 kv = ld(Kb, ks, krow, cc, m);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) dot = sa::dot2_bf16(qv[m][w], kv[w], dot);
-      }
-      dot = quad_sum(dot) * c2;
-      y[cc] = (n0 + cc < n1 && ok[cc]) ? dot : -INFINITY;
-    }
-    float mx = y[0];
-#pragma unroll
-    for (int cc = 1; cc < kChunk; ++cc) mx = fmaxf(mx, y[cc]);
-    if (mx > m_run) {  // per query (the quad agrees); rescale the running state
-      const float alpha = sa::fast_exp2(m_run - mx);
-      l_run *= alpha;
-#pragma unroll
-      for (int m = 0; m < C::CPL; ++m)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[m][e] *= alpha;
-      m_run = mx;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-    for (int cc = 0; cc < kChunk; cc += 2) {
-      const uint32_t pp = sa::pack_bf16x2(sa::fast_exp2(y[cc] - m_use), sa::fast_exp2(y[cc + 1] - m_use));
-      l_run = sa::dot2_bf16(pp, 0x3f803f80u, l_run);
-#pragma unroll
-      for (int m = 0; m < C::CPL; ++m) {
-        sa::u32x4 va = ld(Vb, vs, vrow, cc, m);
-        sa::u32x4 vb = ld(Vb, vs, vrow, cc + 1, m);
-        if (MASKED) {  // keys before the sequence start: zero weight and zero value
-          if (!ok[cc]) va = sa::u32x4{0u, 0u, 0u, 0u};
-          if (!ok[cc + 1]) vb = sa::u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          acc[m][2 * w] = sa::dot2_bf16(pp, pair_lo(va[w], vb[w]), acc[m][2 * w]);
-          acc[m][2 * w + 1] = sa::dot2_bf16(pp, pair_hi(va[w], vb[w]), acc[m][2 * w + 1]);
-        }
-      }
+    for (int q = 0; q < C::IPW; ++q) {
+      const int inst = q * C::NW + w;
+      const int row = inst * C::RPI + lane / C::CPR;
+      const int c = swz(lane % C::CPR, row);
+      const int ar = min(max(blk * 64 + row, 0), a.N - 1);
+      const uint32_t dst = lds0 + slot * (64 * ROWB) + inst * 1024;
+      sa::dma16(Kh, (uint32_t)ar * krow + 16u * c, dst);
+      sa::dma16(Vh, (uint32_t)ar * vrow + 16u * c, dst + C::RINGB);
     }
   };
 
-  // near distances from LDS, then far ones from global memory; a chunk needs
-  // masking only if the tile's first query precedes its largest distance
-  for (int n0 = 0; n0 < a.nnear; n0 += kChunk) {
-    const int n1 = min(n0 + kChunk, a.nnear);
-    if (t0 >= a.offs[n1 - 1])
-      chunk(n0, n1, std::false_type{}, std::false_type{});
-    else
-      chunk(n0, n1, std::false_type{}, std::true_type{});
-  }
-  for (int n0 = a.nnear; n0 < a.noff; n0 += kChunk) {
-    const int n1 = min(n0 + kChunk, a.noff);
-    if (t0 >= a.offs[n1 - 1])
-      chunk(n0, n1, std::true_type{}, std::false_type{});
-    else
-      chunk(n0, n1, std::true_type{}, std::true_type{});
-  }
+  sa::u32x4 qb[NC];
+  auto load_q = [&](int ti) {
+    const int tq = min(ti * C::TQ + 16 * w + i, a.N - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qb[c] = sa::gload16(Qh, (uint32_t)tq * qrow + 16u * (4 * c + g));
+  };
 
-  if (!live) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  uint16_t* O = (uint16_t*)a.o + b * a.os[0] + h * a.os[1] + (int64_t)t * a.os[2];
+  // Far batch [n0, n0 + FC) of the far rungs (entries past nfar repeat the last
+  // rung; their weight is 0): K rows, then V rows (2 * FC * NC loads).
+  auto far_load = [&](int n0, int tq, sa::u32x4 (&kf)[FC][NC], sa::u32x4 (&vf)[FC][NC]) {
+    uint32_t src[FC];
 #pragma unroll
-  for (int m = 0; m < C::CPL; ++m) {
-    sa::u32x4 w;
+    for (int n = 0; n < FC; ++n) src[n] = (uint32_t)max(tq - a.offs[a.nnear + min(n0 + n, nfar - 1)], 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = sa::pack_bf16x2(acc[m][2 * e] * inv, acc[m][2 * e + 1] * inv);
-    *(sa::u32x4*)(O + 8 * (j + 4 * m)) = w;
+    for (int n = 0; n < FC; ++n)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[n][c] = sa::gload16(Kh, src[n] * krow + 16u * (4 * c + g));
+#pragma unroll
+    for (int n = 0; n < FC; ++n)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vf[n][c] = sa::gload16(Vh, src[n] * vrow + 16u * (4 * c + g));
+  };
+  auto far_scores = [&](int n0, int tq, sa::u32x4 (&kf)[FC][NC], float (&yf)[FC]) {
+#pragma unroll
+    for (int n = 0; n < FC; ++n) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sa::tie(kf[n][c]);
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dot = sa::dot2_bf16(qb[c][x], kf[n][c][x], dot);
+      dot = sa::sum_xor32(sa::sum_xor16(dot));
+      const bool ok = n0 + n < nfar && tq >= a.offs[a.nnear + min(n0 + n, nfar - 1)];
+      yf[n] = ok ? dot * c2 : -INFINITY;
+    }
+  };
+  sa::f32x4 acc[NDT];
+  float l = 0.f;
+  auto far_pv = [&](const float (&yf)[FC], float mu, sa::u32x4 (&vf)[FC][NC]) {
+#pragma unroll
+    for (int n = 0; n < FC; ++n)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sa::tie(vf[n][c]);
+#pragma unroll
+    for (int n = 0; n < FC; n += 2) {
+      const uint32_t pp = sa::pack_bf16x2(sa::fast_exp2(yf[n] - mu), sa::fast_exp2(yf[n + 1] - mu));
+      l = sa::dot2_bf16(pp, lone, l);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t va = vf[n][c][x], vb = vf[n + 1][c][x];
+          sa::f32x4& o = acc[2 * c + (x >> 1)];
+          o[2 * (x & 1)] = sa::dot2_bf16(pp, pair_lo(va, vb), o[2 * (x & 1)]);
+          o[2 * (x & 1) + 1] = sa::dot2_bf16(pp, pair_hi(va, vb), o[2 * (x & 1) + 1]);
+        }
+    }
+  };
+
+  if (has_near) {
+    stage(ti0 - 1);
+    stage(ti0);
   }
-  if (j == 0) a.lse[((int64_t)b * a.H + h) * a.N + t] = l_run > 0.f ? (m_run + log2f(l_run)) * sa::kLn2 : -INFINITY;
+  load_q(ti0);
+
+  for (int ti = ti0; ti < ti1; ++ti) {
+    sa::vm_wait<0>();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sa::tie(qb[c]);
+    __syncthreads();  // ring blocks ti - 1, ti are in LDS; block ti - 2 is free
+    const int t0 = ti * C::TQ, t = t0 + 16 * w + i, tq = min(t, a.N - 1);
+    const bool dma = has_near && ti + 1 < ti1;
+
+    sa::u32x4 kf[FC][NC], vf[FC][NC];
+    if (nfar > 0) far_load(0, tq, kf, vf);
+    if (dma) stage(ti + 1);
+
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = sa::f32x4{0.f, 0.f, 0.f, 0.f};
+    l = 0.f;
+    float y[20];
+    float mx = -INFINITY;
+    // ring row of band row 0 (the band starts at t0 + 16 w - 64)
+    int rb = (t0 + 16 * w + 128) % C::RING;
+    if (has_near) {
+#pragma unroll
+      for (int kb = 0; kb < 5; ++kb) {
+        int rr = rb + 16 * kb;
+        rr = rr >= C::RING ? rr - C::RING : rr;
+        sa::f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+          const sa::u32x4 kv = *(const sa::u32x4*)(smem + rr * ROWB + kofs[u]);
+          s = sa::mfma16(kv, qb[u], s);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[4 * kb + r] = s[r] * c2;
+      }
+      const uint32_t vm = t0 == 0 ? (nmask & cmask) : nmask;
+#pragma unroll
+      for (int e = 0; e < 20; ++e) {
+        y[e] = ((vm >> e) & 1u) ? y[e] : -INFINITY;
+        mx = fmaxf(mx, y[e]);
+      }
+      mx = sa::max_xor32(sa::max_xor16(mx));
+    }
+    float yf[FC];
+    if (nfar > 0) {
+      if (dma)
+        sa::vm_wait<FC * NC + 2 * C::IPW>();
+      else
+        sa::vm_wait<FC * NC>();
+      far_scores(0, tq, kf, yf);
+#pragma unroll
+      for (int n = 0; n < FC; ++n) mx = fmaxf(mx, yf[n]);
+    }
+    float m = mx;
+    float mu = m == -INFINITY ? 0.f : m;
+    if (has_near) {
+      uint32_t pk[5][2];
+#pragma unroll
+      for (int kb = 0; kb < 5; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          pk[kb][j] = sa::pack_bf16x2(sa::fast_exp2(y[4 * kb + 2 * j] - mu), sa::fast_exp2(y[4 * kb + 2 * j + 1] - mu));
+          l = sa::dot2_bf16(pk[kb][j], 0x3f803f80u, l);
+        }
+#pragma unroll
+      for (int st = 0; st < 3; ++st) {
+        int r0 = rb + 32 * st;
+        r0 = r0 >= C::RING ? r0 - C::RING : r0;
+        int r1 = r0 + 16;
+        r1 = r1 >= C::RING ? r1 - C::RING : r1;
+        const sa::u32x4 bop = {pk[2 * st][0], pk[2 * st][1], st < 2 ? pk[2 * st + 1][0] : 0u,
+                               st < 2 ? pk[2 * st + 1][1] : 0u};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const sa::u32x2 v0 = sa::lds_read_tr16(smem + C::RINGB + r0 * ROWB + vofs[dt]);
+          sa::u32x2 v1 = {0u, 0u};
+          if (st < 2) v1 = sa::lds_read_tr16(smem + C::RINGB + r1 * ROWB + vofs[dt]);
+          acc[dt] = sa::mfma16(sa::u32x4{v0[0], v0[1], v1[0], v1[1]}, bop, acc[dt]);
+        }
+      }
+    }
+    if (nfar > 0) {
+      if (dma)
+        sa::vm_wait<2 * C::IPW>();
+      else
+        sa::vm_wait<0>();
+      far_pv(yf, mu, vf);
+      for (int n0 = FC; n0 < nfar; n0 += FC) {
+        far_load(n0, tq, kf, vf);
+        sa::vm_wait<FC * NC>();
+        far_scores(n0, tq, kf, yf);
+        float mb = yf[0];
+#pragma unroll
+        for (int n = 1; n < FC; ++n) mb = fmaxf(mb, yf[n]);
+        if (mb > m) {  // per query (its 4 lanes agree): rescale the running state
+          const float alpha = sa::fast_exp2(m - mb);
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[dt][r] *= alpha;
+          m = mb;
+        }
+        mu = m == -INFINITY ? 0.f : m;
+        sa::vm_wait<0>();
+        far_pv(yf, mu, vf);
+      }
+    }
+
+    l = sa::sum_xor32(sa::sum_xor16(l));
+    if (t < a.N) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* orow = Oh + (int64_t)t * a.os[2];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const sa::f32x4& o0 = acc[2 * c];
+        const sa::f32x4& o1 = acc[2 * c + 1];
+        const sa::u32x4 wv = {sa::pack_bf16x2(o0[0] * inv, o0[1] * inv), sa::pack_bf16x2(o0[2] * inv, o0[3] * inv),
+                              sa::pack_bf16x2(o1[0] * inv, o1[1] * inv), sa::pack_bf16x2(o1[2] * inv, o1[3] * inv)};
+        *(sa::u32x4*)(orow + 8 * (4 * c + g)) = wv;
+      }
+      if (g == 0) Lh[t] = l > 0.f ? (m + log2f(l)) * sa::kLn2 : -INFINITY;
+    }
+    if (ti + 1 < ti1) load_q(ti + 1);
+  }
 }
 
 template <int D, bool BF16>
@@ -418,21 +543,37 @@ extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k
   a.scale_log2 = scale * sa::kLog2e;
   for (int n = 0; n < num_offsets; ++n) a.offs[n] = offsets[n];
   a.nnear = 0;
-  a.span_r = 0;
-  while (a.nnear < num_offsets && offsets[a.nnear] <= kNearMax) a.span_r = offsets[a.nnear++];
+  a.near_bits = 0;
+  a.near64 = 0;
+  while (a.nnear < num_offsets && offsets[a.nnear] <= kNearMax) {
+    const int x = offsets[a.nnear++];
+    if (x < 64)
+      a.near_bits |= 1ull << x;
+    else
+      a.near64 = 1;
+  }
   if (dtype == SA_BF16) {
+    // rows are addressed with 32-bit byte offsets from the head's base
+    const int64_t rowb = std::max(st[0].s, std::max(st[1].s, st[2].s)) * 2;
+    if ((int64_t)N * rowb > 0xffffffffll) return SA_ERR_UNSUPPORTED;
+    // tiles per workgroup: keep at least ~4 workgroups per slot of the chip
+    // (256 CUs x 3 resident workgroups); a longer walk re-copies fewer halo rows
+    const int64_t ntiles = ((int64_t)N + 63) / 64;
+    const int64_t total = (int64_t)B * H * ntiles;
+    a.tpw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ntiles, total / (4 * 256 * 3)));
+    a.nchunk = (int32_t)((ntiles + a.tpw - 1) / a.tpw);
+    if ((int64_t)B * H * a.nchunk > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)((int64_t)B * H * a.nchunk));
     if (d == 64) {
-      using Cf = OffCfg<64>;
-      static const sa_status lds_ok = allow_lds((const void*)&offset_bf16_kernel<64>, Cf::LDSB);
+      using Cf = MCfg<64>;
+      static const sa_status lds_ok = allow_lds((const void*)&offset_mfma_kernel<64>, Cf::LDSB);
       if (lds_ok != SA_OK) return lds_ok;
-      const dim3 grid((unsigned)((int64_t)B * H * ((N + Cf::TQ - 1) / Cf::TQ)));
-      hipLaunchKernelGGL((offset_bf16_kernel<64>), grid, dim3(Cf::NT), Cf::LDSB, stream, a);
+      hipLaunchKernelGGL((offset_mfma_kernel<64>), grid, dim3(256), Cf::LDSB, stream, a);
     } else {
-      using Cf = OffCfg<128>;
-      static const sa_status lds_ok = allow_lds((const void*)&offset_bf16_kernel<128>, Cf::LDSB);
+      using Cf = MCfg<128>;
+      static const sa_status lds_ok = allow_lds((const void*)&offset_mfma_kernel<128>, Cf::LDSB);
       if (lds_ok != SA_OK) return lds_ok;
-      const dim3 grid((unsigned)((int64_t)B * H * ((N + Cf::TQ - 1) / Cf::TQ)));
-      hipLaunchKernelGGL((offset_bf16_kernel<128>), grid, dim3(Cf::NT), Cf::LDSB, stream, a);
+      hipLaunchKernelGGL((offset_mfma_kernel<128>), grid, dim3(256), Cf::LDSB, stream, a);
     }
   } else {
     const dim3 grid((unsigned)((int64_t)B * H * tiles));

@@ -45,6 +45,13 @@ __device__ __forceinline__ f32x16 mfma32_z(u32x4 a, u32x4 b) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), z, 0, 0, 0);
 }
 
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds row l%16 of A
+// and column l%16 of B at k = 8(l/16) .. 8(l/16)+7, and column l%16 of D at
+// rows 4(l/16) .. 4(l/16)+3.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014): advance by the
@@ -74,6 +81,43 @@ __device__ __forceinline__ float max_xor32(float x) {
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// max / sum of x over lanes l and l ^ 16 (v_permlane16_swap exchanges rows of
+// 16 lanes pairwise: row 0 <-> row 1, row 2 <-> row 3).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// 16-byte global load issued as inline asm (sbase: wave-uniform base pointer,
+// voff: per-lane byte offset).  The compiler does not count it, so the caller
+// waits for it with vm_wait<n>() (n = vector memory operations issued after it
+// that may stay outstanding) and then tie()s the result, which orders every use
+// after the wait.
+__device__ __forceinline__ u32x4 gload16(const void* sbase, uint32_t voff) {
+  u32x4 r;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sbase) : "memory");
+#else
+  r = u32x4{0u, 0u, 0u, 0u};
+#endif
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#endif
+}
+__device__ __forceinline__ void tie(u32x4& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
 }
 
 // Direct global -> LDS copies (global_load_lds_dwordx4): each lane's 16 bytes

@@ -100,3 +100,61 @@ def test_gqa_offsets():
     torch.cuda.synchronize()
     o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 0.125)
     compare(o, lse, o_ref, l_ref, torch.bfloat16, "gqa")
+
+
+# Tables that exercise each part of the bf16 kernel on their own: only far
+# rungs (> 64, no staged band), only near distances, distance 64 at the band's
+# edge, a dense table whose 60+ far rungs take many register batches, and rows
+# that stay empty (smallest distance > 0).
+TABLE_CASES = {
+    "far-only": [65, 100, 299],
+    "near-only": list(range(9)),
+    "edge-64": [64],
+    "near-far-edge": [0, 63, 64, 65],
+    "dense": list(range(120)),
+    "sparse-near": [1, 7, 30, 57],
+}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("name", sorted(TABLE_CASES))
+def test_table_shapes_bf16(name, d):
+    require_gpu()
+    N = 300
+    offs = TABLE_CASES[name]
+    q, k, v = wl.make_qkv(2, 3, N, d, torch.bfloat16, 700 + len(offs) + d)
+    announce(f"[offset] table {name} d={d}")
+    o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs, 0.1)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 0.1)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, f"table {name} d={d}")
+
+
+def test_strided_layout_and_negative_scale():
+    """Q / K / V / O as [B, N, H, d] storage viewed as [B, H, N, d]."""
+    require_gpu()
+    B, H, N, d = 2, 4, 700, 64
+    g = torch.Generator().manual_seed(77)
+    store = [torch.randn(B, N, H, d, generator=g).to(torch.bfloat16) for _ in range(3)]
+    q, k, v = [t.cuda().permute(0, 2, 1, 3) for t in store]
+    offs = _table(1.7, N)
+    announce("[offset] strided [B,N,H,d] layout, scale -0.125")
+    o, lse = api.offset_attn_fwd(q, k, v, offs, -0.125)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oo.offset_attention(f64(q.cpu()), f64(k.cpu()), f64(v.cpu()), offs, -0.125)
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, "strided")
+
+
+def test_multi_tile_walk_ragged():
+    """Enough (batch, head, tile) work that each workgroup walks several
+    64-query tiles through the staged ring; N is not a multiple of 64, so the
+    last walk of every head is shorter."""
+    require_gpu()
+    B, H, N, d = 4, 24, 4100, 64
+    offs = _table(1.25, N)
+    q, k, v = wl.make_qkv(B, H, N, d, torch.bfloat16, 4100)
+    announce(f"[offset] multi-tile walk {B}x{H}x{N}x{d}")
+    o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 1 / math.sqrt(d))
+    compare(o, lse, o_ref, l_ref, torch.bfloat16, "walk")
