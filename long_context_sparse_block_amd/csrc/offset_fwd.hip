@@ -10,17 +10,22 @@
 //     scores S^T = K Q^T and the product O^T += V^T P^T run on
 //     v_mfma_f32_16x16x32_bf16 over the whole band; entries whose distance is
 //     not in the table get weight 0 (a per-lane bit mask).  K / V rows reach
-//     LDS through a ring of three 64-row blocks filled by direct global->LDS
-//     copies, the next tile's block in flight while the current one is used;
-//     each row is copied once per workgroup.
+//     LDS by direct global->LDS copies into a ring of 64-row blocks: two when
+//     a workgroup has one tile, three when it walks several (the next tile's
+//     block is then in flight while the current one is used); each row is
+//     copied once per workgroup.
 //   * far rungs (> 64): each row is used by one query of the tile, so it is
-//     gathered straight into registers (no LDS round trip), four rungs at a
-//     time, with an online-softmax rescale per batch.  The lane layout is the
-//     MFMA output layout: lane l holds query l % 16 and the head-dimension
-//     entries d = 32 c + 8 (l / 16) + e (e < 8), i.e. 16-byte chunks 4 c + l/16
-//     of a row; the O^T tiles take their rows in that permuted d order, so the
-//     far contributions accumulate into the same registers.  A rung's dot
-//     product is reduced over the 4 lanes of a query with two lane-row swaps.
+//     gathered straight into registers (no LDS round trip), two rungs at a
+//     time with an online-softmax rescale per batch; the K rows of batch b + 1
+//     are in flight while the V rows of batch b are used.  The gather runs in
+//     a layout of its own where the 4 lanes reading one row are adjacent
+//     (lane 4 q + j: query q, 16-byte chunks 4 c + j), so each group of 4 lanes
+//     reads one 64-byte segment; the MFMA layout has those lanes 16 apart,
+//     which costs about 3x in L2 gather throughput.  The two layouts hold the
+//     same (query, chunks) per lane up to the lane permutation 16 j + q <->
+//     4 q + j, so q and the band's O^T state move across with ds_bpermute
+//     once per tile; the O^T tiles take their rows in the permuted d order
+//     that makes a lane's entries its gathered chunks.
 //   * all global loads of the loop are issued as inline asm and waited for
 //     with explicit vmcnt counts, so waiting for a far batch never waits for
 //     the ring copies issued after it.
@@ -127,12 +132,22 @@ __device__ __forceinline__ int swz(int c, int row) {
   return c ^ ((r & 1) | ((r & 2) << 1) | ((r & 4) >> 1));
 }
 
-template <int D>
+#ifndef SA_OFF_FC64
+#define SA_OFF_FC64 2
+#endif
+#ifndef SA_OFF_TPW_DIV
+#define SA_OFF_TPW_DIV 4
+#endif
+#ifndef SA_OFF_WAVES64
+#define SA_OFF_WAVES64 3
+#endif
+
+template <int D, int NS>
 struct MCfg {
   static constexpr int NW = 4;               // waves per workgroup
   static constexpr int TQ = 64;              // queries per tile step (16 per wave)
   static constexpr int ROWB = 2 * D;         // bytes per K / V row
-  static constexpr int RING = 192;           // staged rows: three 64-row blocks
+  static constexpr int RING = 64 * NS;       // staged rows: NS blocks of 64 rows
   static constexpr int RINGB = RING * ROWB;  // bytes of the K ring (the V ring follows)
   static constexpr int LDSB = 2 * RINGB;
   static constexpr int NC = D / 32;          // 16-byte chunks a lane holds per row
@@ -140,12 +155,12 @@ struct MCfg {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;    // rows per copy wave-instruction
   static constexpr int IPW = ROWB / 64;      // copy wave-instructions per wave, block and matrix
-  static constexpr int FC = D == 64 ? 4 : 2; // far rungs per register batch (even)
+  static constexpr int FC = D == 64 ? SA_OFF_FC64 : 2;  // far rungs per register batch (even)
 };
 
-template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffArgs a) {
-  using C = MCfg<D>;
+template <int D, int NS>
+__global__ __launch_bounds__(256, D == 64 ? SA_OFF_WAVES64 : 2) void offset_mfma_kernel(OffArgs a) {
+  using C = MCfg<D, NS>;
   constexpr int NC = C::NC, NDT = C::NDT, FC = C::FC, ROWB = C::ROWB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const uint32_t lds0 = sa::lds_addr(smem);
@@ -167,7 +182,6 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
   const bool has_near = a.nnear > 0;
   const int nfar = a.noff - a.nnear;
   const float c2 = a.scale_log2;
-  const uint32_t lone = g == 0 ? 0x3f803f80u : 0u;  // far weights are counted once per query
 
   // Band row of this lane's score (block kb, entry r): 16 kb + 4 g + r; its
   // distance from query i is 64 + i - (16 kb + 4 g + r).  nmask: the distance
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
   // outside [0, N) are clamped to a valid row: they only meet zero weights.
   // Every wave issues exactly 2 * IPW copies.
   auto stage = [&](int blk) {
-    const uint32_t slot = (uint32_t)((blk + 3) % 3);
+    const uint32_t slot = (uint32_t)((blk + NS) % NS);
 #pragma unroll
     for (int q = 0; q < C::IPW; ++q) {
       const int inst = q * C::NW + w;
@@ -212,29 +226,34 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
     }
   };
 
-  sa::u32x4 qb[NC];
+  // Far-rung layout: lane 4 fq + fj holds query fq of the wave and chunks
+  // 4 c + fj, so the 4 lanes that read one row are adjacent (one 64-byte
+  // segment per group of 4 lanes).  It holds the same (query, chunks) as lane
+  // 16 fj + fq of the MFMA layout: the two differ by a lane permutation.
+  const int fq = lane >> 2, fj = lane & 3;
+  const int to_far = (16 * fj + fq) * 4;  // bpermute address: MFMA layout -> far layout
+  const int to_mfma = (4 * i) * 4;        // far layout -> MFMA layout (quad-uniform values)
+  const uint32_t lone = fj == 0 ? 0x3f803f80u : 0u;  // far weights are counted once per query
+
+  sa::u32x4 qb[NC], qf[NC];  // q in the MFMA layout (B operand) and in the far layout
   auto load_q = [&](int ti) {
     const int tq = min(ti * C::TQ + 16 * w + i, a.N - 1);
 #pragma unroll
     for (int c = 0; c < NC; ++c) qb[c] = sa::gload16(Qh, (uint32_t)tq * qrow + 16u * (4 * c + g));
   };
 
-  // Far batch [n0, n0 + FC) of the far rungs (entries past nfar repeat the last
-  // rung; their weight is 0): K rows, then V rows (2 * FC * NC loads).
-  auto far_load = [&](int n0, int tq, sa::u32x4 (&kf)[FC][NC], sa::u32x4 (&vf)[FC][NC]) {
+  // Rows of far batch [n0, n0 + FC) of the far rungs from K or V (entries past
+  // nfar repeat the last rung; their weight is 0): FC * NC loads.
+  auto far_rows = [&](int n0, int tqf, const char* base, uint32_t rowb, sa::u32x4 (&buf)[FC][NC]) {
     uint32_t src[FC];
 #pragma unroll
-    for (int n = 0; n < FC; ++n) src[n] = (uint32_t)max(tq - a.offs[a.nnear + min(n0 + n, nfar - 1)], 0);
+    for (int n = 0; n < FC; ++n) src[n] = (uint32_t)max(tqf - a.offs[a.nnear + min(n0 + n, nfar - 1)], 0);
 #pragma unroll
     for (int n = 0; n < FC; ++n)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kf[n][c] = sa::gload16(Kh, src[n] * krow + 16u * (4 * c + g));
-#pragma unroll
-    for (int n = 0; n < FC; ++n)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) vf[n][c] = sa::gload16(Vh, src[n] * vrow + 16u * (4 * c + g));
+      for (int c = 0; c < NC; ++c) buf[n][c] = sa::gload16(base, src[n] * rowb + 16u * (4 * c + fj));
   };
-  auto far_scores = [&](int n0, int tq, sa::u32x4 (&kf)[FC][NC], float (&yf)[FC]) {
+  auto far_scores = [&](int n0, int tqf, sa::u32x4 (&kf)[FC][NC], float (&yf)[FC]) {
 #pragma unroll
     for (int n = 0; n < FC; ++n) {
 #pragma unroll
@@ -243,12 +262,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) dot = sa::dot2_bf16(qb[c][x], kf[n][c][x], dot);
-      dot = sa::sum_xor32(sa::sum_xor16(dot));
-      const bool ok = n0 + n < nfar && tq >= a.offs[a.nnear + min(n0 + n, nfar - 1)];
+        for (int x = 0; x < 4; ++x) dot = sa::dot2_bf16(qf[c][x], kf[n][c][x], dot);
+      dot = sa::quad_sum(dot);
+      const int dn = a.offs[a.nnear + min(n0 + n, nfar - 1)];
+      const bool ok = (n0 + n < nfar) & (tqf >= dn);
       yf[n] = ok ? dot * c2 : -INFINITY;
     }
   };
+  // O^T accumulators: MFMA layout during the band, far layout afterwards.
+  // Entry [dt][r] is d = 8 (4 (dt/2) + lane chunk) + 4 (dt%2) + r.
   sa::f32x4 acc[NDT];
   float l = 0.f;
   auto far_pv = [&](const float (&yf)[FC], float mu, sa::u32x4 (&vf)[FC][NC]) {
@@ -281,22 +303,30 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
   for (int ti = ti0; ti < ti1; ++ti) {
     sa::vm_wait<0>();
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sa::tie(qb[c]);
+    for (int c = 0; c < NC; ++c) {
+      sa::tie(qb[c]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qf[c][x] = __float_as_uint(sa::bperm(to_far, __uint_as_float(qb[c][x])));
+    }
     __syncthreads();  // ring blocks ti - 1, ti are in LDS; block ti - 2 is free
-    const int t0 = ti * C::TQ, t = t0 + 16 * w + i, tq = min(t, a.N - 1);
-    const bool dma = has_near && ti + 1 < ti1;
+    const int t0 = ti * C::TQ;
+    const int tf = t0 + 16 * w + fq, tqf = min(tf, a.N - 1);
+    const bool dma = NS == 3 && has_near && ti + 1 < ti1;
 
     sa::u32x4 kf[FC][NC], vf[FC][NC];
-    if (nfar > 0) far_load(0, tq, kf, vf);
+    if (nfar > 0) {
+      far_rows(0, tqf, Kh, krow, kf);
+      far_rows(0, tqf, Vh, vrow, vf);
+    }
     if (dma) stage(ti + 1);
 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = sa::f32x4{0.f, 0.f, 0.f, 0.f};
     l = 0.f;
     float y[20];
-    float mx = -INFINITY;
+    float mx = -INFINITY;  // MFMA layout, per query
     // ring row of band row 0 (the band starts at t0 + 16 w - 64)
-    int rb = (t0 + 16 * w + 128) % C::RING;
+    const int rb = (t0 + 16 * w + C::RING - 64) % C::RING;
     if (has_near) {
 #pragma unroll
       for (int kb = 0; kb < 5; ++kb) {
@@ -325,20 +355,25 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
         sa::vm_wait<FC * NC + 2 * C::IPW>();
       else
         sa::vm_wait<FC * NC>();
-      far_scores(0, tq, kf, yf);
+      far_scores(0, tqf, kf, yf);
+      float mf = yf[0];
 #pragma unroll
-      for (int n = 0; n < FC; ++n) mx = fmaxf(mx, yf[n]);
+      for (int n = 1; n < FC; ++n) mf = fmaxf(mf, yf[n]);
+      mx = fmaxf(mx, sa::bperm(to_mfma, mf));
     }
-    float m = mx;
+    // running max, the same value in both layouts
+    float m = sa::bperm(to_far, mx);
     float mu = m == -INFINITY ? 0.f : m;
     if (has_near) {
+      const float muc = mx == -INFINITY ? 0.f : mx;
       uint32_t pk[5][2];
+      float ln = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 5; ++kb)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          pk[kb][j] = sa::pack_bf16x2(sa::fast_exp2(y[4 * kb + 2 * j] - mu), sa::fast_exp2(y[4 * kb + 2 * j + 1] - mu));
-          l = sa::dot2_bf16(pk[kb][j], 0x3f803f80u, l);
+          pk[kb][j] = sa::pack_bf16x2(sa::fast_exp2(y[4 * kb + 2 * j] - muc), sa::fast_exp2(y[4 * kb + 2 * j + 1] - muc));
+          ln = sa::dot2_bf16(pk[kb][j], 0x3f803f80u, ln);
         }
 #pragma unroll
       for (int st = 0; st < 3; ++st) {
@@ -356,17 +391,38 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
           acc[dt] = sa::mfma16(sa::u32x4{v0[0], v0[1], v1[0], v1[1]}, bop, acc[dt]);
         }
       }
+      // band state -> far layout
+      ln = sa::sum_xor32(sa::sum_xor16(ln));
+      l = sa::bperm(to_far, ln);
+      l = fj == 0 ? l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][r] = sa::bperm(to_far, acc[dt][r]);
     }
+    // Far batches, software-pipelined by one half: K of batch b + 1 is in
+    // flight while V of batch b is used, and V of batch b + 1 while the scores
+    // of batch b + 1 are formed (queue order: K0 V0 [copies] K1 V1 K2 ...).
     if (nfar > 0) {
-      if (dma)
-        sa::vm_wait<2 * C::IPW>();
-      else
-        sa::vm_wait<0>();
-      far_pv(yf, mu, vf);
-      for (int n0 = FC; n0 < nfar; n0 += FC) {
-        far_load(n0, tq, kf, vf);
+      for (int n0 = 0; n0 < nfar; n0 += FC) {
+        const bool more = n0 + FC < nfar;
+        if (more) far_rows(n0 + FC, tqf, Kh, krow, kf);
+        if (n0 == 0 && dma) {
+          if (more)
+            sa::vm_wait<2 * C::IPW + FC * NC>();
+          else
+            sa::vm_wait<2 * C::IPW>();
+        } else {
+          if (more)
+            sa::vm_wait<FC * NC>();
+          else
+            sa::vm_wait<0>();
+        }
+        far_pv(yf, mu, vf);
+        if (!more) break;
+        far_rows(n0 + FC, tqf, Vh, vrow, vf);
         sa::vm_wait<FC * NC>();
-        far_scores(n0, tq, kf, yf);
+        far_scores(n0 + FC, tqf, kf, yf);
         float mb = yf[0];
 #pragma unroll
         for (int n = 1; n < FC; ++n) mb = fmaxf(mb, yf[n]);
@@ -380,24 +436,22 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void offset_mfma_kernel(OffAr
           m = mb;
         }
         mu = m == -INFINITY ? 0.f : m;
-        sa::vm_wait<0>();
-        far_pv(yf, mu, vf);
       }
     }
 
-    l = sa::sum_xor32(sa::sum_xor16(l));
-    if (t < a.N) {
+    l = sa::quad_sum(l);
+    if (tf < a.N) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* orow = Oh + (int64_t)t * a.os[2];
+      uint16_t* orow = Oh + (int64_t)tf * a.os[2];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const sa::f32x4& o0 = acc[2 * c];
         const sa::f32x4& o1 = acc[2 * c + 1];
         const sa::u32x4 wv = {sa::pack_bf16x2(o0[0] * inv, o0[1] * inv), sa::pack_bf16x2(o0[2] * inv, o0[3] * inv),
                               sa::pack_bf16x2(o1[0] * inv, o1[1] * inv), sa::pack_bf16x2(o1[2] * inv, o1[3] * inv)};
-        *(sa::u32x4*)(orow + 8 * (4 * c + g)) = wv;
+        *(sa::u32x4*)(orow + 8 * (4 * c + fj)) = wv;
       }
-      if (g == 0) Lh[t] = l > 0.f ? (m + log2f(l)) * sa::kLn2 : -INFINITY;
+      if (fj == 0) Lh[tf] = l > 0.f ? (m + log2f(l)) * sa::kLn2 : -INFINITY;
     }
     if (ti + 1 < ti1) load_q(ti + 1);
   }
@@ -486,6 +540,15 @@ __global__ __launch_bounds__(kThreads) void offset_fwd_kernel(OffArgs a) {
   a.lse[((int64_t)b * a.H + h) * a.N + t] = l > 0.f ? (m + log2f(l)) * sa::kLn2 : -INFINITY;
 }
 
+template <int D, int NS>
+sa_status launch_mfma(const OffArgs& a, dim3 grid, hipStream_t stream) {
+  using Cf = MCfg<D, NS>;
+  static const sa_status lds_ok = allow_lds((const void*)&offset_mfma_kernel<D, NS>, Cf::LDSB);
+  if (lds_ok != SA_OK) return lds_ok;
+  hipLaunchKernelGGL((offset_mfma_kernel<D, NS>), grid, dim3(256), Cf::LDSB, stream, a);
+  return SA_OK;
+}
+
 }  // namespace
 
 extern "C" sa_status offset_attn_make_table(int32_t W, double alpha, const int64_t* base, int32_t K,
@@ -560,21 +623,20 @@ extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k
     // (256 CUs x 3 resident workgroups); a longer walk re-copies fewer halo rows
     const int64_t ntiles = ((int64_t)N + 63) / 64;
     const int64_t total = (int64_t)B * H * ntiles;
-    a.tpw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ntiles, total / (4 * 256 * 3)));
+    a.tpw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ntiles, total / (SA_OFF_TPW_DIV * 256 * 3)));
+#ifdef SA_OFF_TPW_FORCE
+    a.tpw = (int32_t)std::min<int64_t>(ntiles, SA_OFF_TPW_FORCE);
+#endif
     a.nchunk = (int32_t)((ntiles + a.tpw - 1) / a.tpw);
     if ((int64_t)B * H * a.nchunk > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((int64_t)B * H * a.nchunk));
-    if (d == 64) {
-      using Cf = MCfg<64>;
-      static const sa_status lds_ok = allow_lds((const void*)&offset_mfma_kernel<64>, Cf::LDSB);
-      if (lds_ok != SA_OK) return lds_ok;
-      hipLaunchKernelGGL((offset_mfma_kernel<64>), grid, dim3(256), Cf::LDSB, stream, a);
-    } else {
-      using Cf = MCfg<128>;
-      static const sa_status lds_ok = allow_lds((const void*)&offset_mfma_kernel<128>, Cf::LDSB);
-      if (lds_ok != SA_OK) return lds_ok;
-      hipLaunchKernelGGL((offset_mfma_kernel<128>), grid, dim3(256), Cf::LDSB, stream, a);
-    }
+    // two ring slots when every workgroup has one tile (no block is prefetched)
+    sa_status ls;
+    if (d == 64)
+      ls = a.tpw == 1 ? launch_mfma<64, 2>(a, grid, stream) : launch_mfma<64, 3>(a, grid, stream);
+    else
+      ls = a.tpw == 1 ? launch_mfma<128, 2>(a, grid, stream) : launch_mfma<128, 3>(a, grid, stream);
+    if (ls != SA_OK) return ls;
   } else {
     const dim3 grid((unsigned)((int64_t)B * H * tiles));
     if (d == 64)

@@ -94,6 +94,18 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Value of x in lane byte_addr / 4 (ds_bpermute: LDS crossbar, no LDS memory).
+__device__ __forceinline__ float bperm(int byte_addr, float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(x)));
+}
+
+// Sum over the 4 lanes of a quad (DPP quad permutes).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
+
 // 16-byte global load issued as inline asm (sbase: wave-uniform base pointer,
 // voff: per-lane byte offset).  The compiler does not count it, so the caller
 // waits for it with vm_wait<n>() (n = vector memory operations issued after it
