@@ -9,6 +9,13 @@ d_k = alpha * f_k of the Fibonacci base; the distances are shared by all
 queries (shifted gathers).  Integer distances are taken as floor(alpha*f + 1/2)
 (round half up), rungs are the base values below N, repeated distances count
 once (the attended set is a set) and distances >= N are dropped.
+
+The same section's variants: the reach-matched power-of-2 base ("Control
+base"), alpha as an exact ratio (the linear stagger alpha = 0.5 + l/(L - 1)
+puts some rungs exactly on a half), and the interpolated gather for a
+continuous d_k = alpha f_k ("Attended set"; "Implementation note"): the
+gathered key and value are the linear interpolation between the rows at
+distances floor(d_k) and floor(d_k) + 1.
 """
 
 import math
@@ -92,4 +99,90 @@ def offset_attention_rows(q, k, v, offsets, scale, samples):
         e = np.exp(s - m)
         o[n] = (e @ v[b, kh, src]) / e.sum()
         lse[n] = m + np.log(e.sum())
+    return o, lse
+
+
+def power2_base(limit):
+    """Powers of two 1, 2, 4, ... below ``limit`` (Sec. 2, "Control base": the
+    log-sparse base that reaches as far as the Fibonacci one with fewer rungs)."""
+    out = []
+    x = 1
+    while x < limit:
+        out.append(x)
+        x *= 2
+    return out
+
+
+def offset_table_ratio(W, num, den, base, N):
+    """offset_table for alpha = num / den held exactly: floor(num f / den + 1/2)
+    evaluated in integers, so a rung that lands exactly on a half rounds up."""
+    d = set(range(0, W + 1))
+    for f in base:
+        d.add((2 * num * f + den) // (2 * den))
+    return sorted(x for x in d if 0 <= x < N)
+
+
+def interp_split(W, alpha, base, N):
+    """Key set of the interpolated gather (Sec. 2, "Attended set"): the window
+    {0..W}, every rung whose alpha*f (double) is an integer as an ordinary
+    distance (so integer alpha*f gives exactly offset_table), and every other
+    rung as (a, w) = (floor(alpha f), alpha f - floor(alpha f)): the key and
+    value are (1 - w) row[t - a] + w row[t - a - 1], used by queries t >= a + 1.
+    Rungs with a + 1 > N - 1 reach no query and are dropped."""
+    ints = set(range(0, W + 1))
+    rungs = []
+    for f in base:
+        x = float(alpha) * float(f)
+        a = math.floor(x)
+        if x == a:
+            ints.add(int(a))
+        elif a + 1 <= N - 1:
+            rungs.append((int(a), x - a))
+    return sorted(i for i in ints if 0 <= i < N), rungs
+
+
+def interp_offset_attention(q, k, v, offsets, rungs, scale):
+    """o, lse for every query over the integer distances ``offsets`` and the
+    interpolated rungs ``rungs`` [(a, w)] (one key each, valid for t >= a + 1).
+
+    q [B, H, N, d], k, v [B, H_kv, N, d] float64.  Returns (o, lse) float64.
+    """
+    B, H, N, d = q.shape
+    rep = H // k.shape[1]
+    offs = list(offsets)
+    R = len(rungs)
+    D = len(offs) + R
+    o = np.zeros((B, H, N, d))
+    lse = np.full((B, H, N), -np.inf)
+    t = np.arange(N)
+
+    def key_rows(kv, b, kh, n):
+        # rows of key n for every query (index arrays ok), as float64 [n_ok, d]
+        if n < len(offs):
+            src = t - offs[n]
+            ok = src >= 0
+            return ok, kv[b, kh, src[ok]]
+        a, w = rungs[n - len(offs)]
+        ok = t - a - 1 >= 0
+        return ok, (1.0 - w) * kv[b, kh, (t - a)[ok]] + w * kv[b, kh, (t - a - 1)[ok]]
+
+    for b in range(B):
+        for h in range(H):
+            kh = h // rep
+            s = np.full((N, D), -np.inf)
+            for n in range(D):
+                ok, kr = key_rows(k, b, kh, n)
+                s[ok, n] = scale * np.einsum("ij,ij->i", q[b, h, t[ok]], kr)
+            m = s.max(axis=1)
+            empty = ~np.isfinite(m)
+            m_safe = np.where(empty, 0.0, m)
+            e = np.where(np.isfinite(s), np.exp(s - m_safe[:, None]), 0.0)
+            l = e.sum(axis=1)
+            acc = np.zeros((N, d))
+            for n in range(D):
+                ok, vr = key_rows(v, b, kh, n)
+                acc[ok] += e[ok, n][:, None] * vr
+            nz = l > 0
+            o[b, h, nz] = acc[nz] / l[nz][:, None]
+            lse[b, h, nz] = m_safe[nz] + np.log(l[nz])
     return o, lse

@@ -51,3 +51,26 @@ def offsets_allowed(offsets):
     def allowed(t, s):
         return (t - s) in offs
     return allowed
+
+
+def explicit_keys_attention(q, keys, values, scale):
+    """Softmax attention of one query over an explicit list of key / value
+    vectors, in pure Python loops (no numpy reductions).  Returns (o, lse);
+    an empty list gives o = 0 and lse = -inf."""
+    d = len(q)
+    if not keys:
+        return [0.0] * d, -math.inf
+    sc = []
+    for kv in keys:
+        acc = 0.0
+        for x in range(d):
+            acc += q[x] * kv[x]
+        sc.append(scale * acc)
+    m = max(sc)
+    ws = [math.exp(x - m) for x in sc]
+    tot = sum(ws)
+    o = [0.0] * d
+    for wgt, vv in zip(ws, values):
+        for x in range(d):
+            o[x] += wgt * vv[x]
+    return [x / tot for x in o], m + math.log(tot)
