@@ -12,9 +12,8 @@ import pytest
 from oracle import offsets as oo
 from oracle import tiny
 
-pytestmark = pytest.mark.cpu
-
 FIB15 = [1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987]
+
 
 def test_power2_base_reach_and_count():
     # powers of two below the limit: 1..512 below 1024, ceil(log2 N) rungs
