@@ -8,7 +8,9 @@
  *   sparse_attn_fwd          block-sparse attention over a CSR mask
  *   offset_attn_fwd          token-level attention over a table of distances
  *
- * and two host helpers (sparse_attn_mask_capacity, offset_attn_make_table).
+ * and the offset_attn_fwd_interp variant, with host helpers
+ * (sparse_attn_mask_capacity, sparse_attn_literal_flags, offset_attn_make_table,
+ * offset_attn_make_table_ratio, offset_attn_make_interp).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -66,6 +68,7 @@ enum {
 #define SA_MAX_RANDOM 32   /* random blocks per row                        */
 #define SA_MAX_BLOCKS 16384 /* blocks per sequence (num_blocks)            */
 #define SA_MAX_OFFSETS 128 /* distances per offset table                   */
+#define SA_MAX_RUNGS 64    /* interpolated rungs per offset call            */
 
 /*
  * Block mask description (HOST struct, passed by host pointer).
@@ -234,6 +237,40 @@ sa_status offset_attn_make_table(int32_t W, double alpha, const int64_t* base, i
                                  int32_t* table_out, int32_t capacity, int32_t* count_out);
 
 /*
+ * The same table with alpha = num / den held exactly (e.g. the linear stagger
+ * alpha = 0.5 + l / (L - 1) of the same page, Sec. 2, "The per-layer
+ * scalar", as (L - 1 + 2 l) / (2 (L - 1))): each rung is
+ * floor(num * base[k] / den + 1/2) computed in integers, so rungs that land
+ * exactly on a half round up, which a double-precision alpha cannot promise.
+ *   0 <= num < 2^31, 1 <= den < 2^31, 0 <= base[k] < 2^31 (else SA_ERR_INVALID)
+ */
+sa_status offset_attn_make_table_ratio(int32_t W, int64_t num, int64_t den, const int64_t* base,
+                                       int32_t K, int32_t N, int32_t* table_out, int32_t capacity,
+                                       int32_t* count_out);
+
+/*
+ * Split of the key set for the interpolated gather of continuous distances
+ * d_k = alpha * base[k] (same page, Sec. 2, "Attended set" and
+ * "Implementation note": the key / value of a rung is the linear
+ * interpolation between the rows at distances floor(d_k) and floor(d_k) + 1).
+ * Host only.
+ *   table_out  HOST int32 [capacity]: ascending distinct integer distances:
+ *              {0..W} and every rung whose d_k (double) is an integer, in [0, N)
+ *   rung_floor HOST int32 [rung_capacity], rung_weight HOST float
+ *              [rung_capacity]: the other rungs in base order as
+ *              (a, w) = (floor(d_k), d_k - floor(d_k)), 0 < w < 1; a rung with
+ *              a + 1 > N - 1 reaches no query and is dropped, and so is a
+ *              negative d_k
+ *   count_out, rung_count  HOST int32: sizes written
+ * With every d_k an integer the table equals offset_attn_make_table's.
+ * SA_ERR_CAPACITY if either output does not fit (nothing written).
+ */
+sa_status offset_attn_make_interp(int32_t W, double alpha, const int64_t* base, int32_t K, int32_t N,
+                                  int32_t* table_out, int32_t capacity, int32_t* count_out,
+                                  int32_t* rung_floor, float* rung_weight, int32_t rung_capacity,
+                                  int32_t* rung_count);
+
+/*
  * Offset attention forward: query t attends keys {t - delta : delta in
  * offsets, t - delta >= 0} (same page, Sec. 2: shifted gathers shared by all
  * queries; the self distance 0 keeps every key set non-empty).
@@ -246,12 +283,32 @@ sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k, const voi
                           const int64_t* strides, const int32_t* offsets, int32_t num_offsets,
                           float scale, hipStream_t stream);
 
+/*
+ * Offset attention with interpolated rungs (same page, Sec. 2, "Attended
+ * set"): query t attends keys {t - delta : delta in offsets, t - delta >= 0}
+ * and, for each rung r with t >= rung_floor[r] + 1, one more key / value
+ *   (1 - w) row[t - a] + w row[t - a - 1],  a = rung_floor[r], w = rung_weight[r]
+ * of K and V (each rung is its own key, also where it meets an integer
+ * distance).  Rungs may come in any order.
+ *   offsets     HOST int32 [num_offsets] as for offset_attn_fwd, but
+ *               0 <= num_offsets <= SA_MAX_OFFSETS
+ *   rung_floor  HOST int32 [num_rungs], 0 <= a and a + 1 <= N - 1
+ *   rung_weight HOST float [num_rungs], 0 <= w <= 1
+ *   0 <= num_rungs <= SA_MAX_RUNGS, num_offsets + num_rungs >= 1
+ * Other arguments, outputs and errors as for offset_attn_fwd.
+ */
+sa_status offset_attn_fwd_interp(int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                 const int64_t* strides, const int32_t* offsets, int32_t num_offsets,
+                                 const int32_t* rung_floor, const float* rung_weight, int32_t num_rungs,
+                                 float scale, hipStream_t stream);
+
 const char* sa_status_string(sa_status s);
 const char* sa_last_hip_error(void);
 int32_t sa_version(void);
 
-/* Layout of sa_mask_desc for bindings: writes min(n, 15) values -- sizeof,
- * then the offset of each field in declaration order -- and returns 15. */
+/* Layout of sa_mask_desc for bindings: writes min(n, 18) values -- sizeof,
+ * then the offset of each field in declaration order -- and returns 18. */
 int32_t sa_mask_desc_layout(int64_t* out, int32_t n);
 
 #ifdef __cplusplus

@@ -1,7 +1,7 @@
 """MI355X (gfx950) sparse block / offset attention: HIP kernels behind a C ABI.
 
 The library (lib/libsparse_attn.so, built by ``build.py``) exports
-sparse_attn_build_mask, sparse_attn_fwd and offset_attn_fwd; ``api`` binds them
+sparse_attn_build_mask, sparse_attn_fwd, offset_attn_fwd and offset_attn_fwd_interp; ``api`` binds them
 for PyTorch tensors.  ``workloads`` holds the seeded synthetic inputs.
 """
 
@@ -11,8 +11,13 @@ from .api import (  # noqa: F401
     fibonacci_base,
     head_group_spec,
     mask_preset,
+    alpha_schedule,
     offset_attn_fwd,
+    offset_attn_fwd_interp,
+    offset_attn_make_interp,
     offset_attn_make_table,
+    offset_attn_make_table_ratio,
+    power2_base,
     sparse_attn_build_mask,
     sparse_attn_check_mask_desc,
     sparse_attn_fwd,

@@ -35,6 +35,7 @@ SA_MAX_RANDOM = 32
 SA_MAX_BLOCKS = 16384
 SA_MAX_OFFSETS = 128
 SA_MAX_PERIOD = 64
+SA_MAX_RUNGS = 64
 
 # every function the header declares, with (restype, argtypes)
 _i32, _i64, _f32, _f64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint64
@@ -75,6 +76,14 @@ SIGNATURES = {
                                       ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
     "offset_attn_fwd": (_i32, [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, _f32, _p]),
+    "offset_attn_make_table_ratio": (_i32, [_i32, _i64, _i64, ctypes.POINTER(_i64), _i32, _i32,
+                                            ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
+    "offset_attn_make_interp": (_i32, [_i32, _f64, ctypes.POINTER(_i64), _i32, _i32, ctypes.POINTER(_i32), _i32,
+                                       ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_f32), _i32,
+                                       ctypes.POINTER(_i32)]),
+    "offset_attn_fwd_interp": (_i32, [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                      ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32),
+                                      ctypes.POINTER(_f32), _i32, _f32, _p]),
     "sa_status_string": (ctypes.c_char_p, [_i32]),
     "sa_last_hip_error": (ctypes.c_char_p, []),
     "sa_version": (_i32, []),

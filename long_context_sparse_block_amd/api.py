@@ -270,6 +270,74 @@ def offset_attn_make_table(W, alpha, base, N):
     return [out[i] for i in range(cnt.value)]
 
 
+def power2_base(limit):
+    """1, 2, 4, 8, ... below ``limit`` (the reach-matched power-of-2 control base)."""
+    out, x = [], 1
+    while x < limit:
+        out.append(x)
+        x *= 2
+    return out
+
+
+def alpha_schedule(kind, L=16, S=7):
+    """Per-layer alpha of the offset pattern: "fixed" (1 everywhere), "linear"
+    (0.5 + l/(L - 1)) or "coprime" (layer l takes the linear value of index
+    S*l mod L)."""
+    lin = [0.5 + l / (L - 1) for l in range(L)]
+    if kind == "fixed":
+        return [1.0] * L
+    if kind == "linear":
+        return lin
+    if kind == "coprime":
+        return [lin[(S * l) % L] for l in range(L)]
+    raise ValueError(kind)
+
+
+def offset_attn_make_table_ratio(W, num, den, base, N):
+    """offset_attn_make_table for alpha = num/den held exactly (C helper)."""
+    K = len(base)
+    b = (ctypes.c_int64 * max(1, K))(*[int(x) for x in base])
+    cap = W + 1 + K
+    out = (ctypes.c_int32 * max(1, cap))()
+    cnt = ctypes.c_int32(0)
+    st = L.lib().offset_attn_make_table_ratio(int(W), int(num), int(den), b, K, int(N), out, cap,
+                                              ctypes.byref(cnt))
+    _check(st, "offset_attn_make_table_ratio")
+    return [out[i] for i in range(cnt.value)]
+
+
+def offset_attn_make_interp(W, alpha, base, N):
+    """(integer distances, [(floor, weight)]) for continuous rungs alpha*f (C helper)."""
+    K = len(base)
+    b = (ctypes.c_int64 * max(1, K))(*[int(x) for x in base])
+    cap = W + 1 + K
+    out = (ctypes.c_int32 * max(1, cap))()
+    rf = (ctypes.c_int32 * max(1, K))()
+    rw = (ctypes.c_float * max(1, K))()
+    cnt, rc = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = L.lib().offset_attn_make_interp(int(W), float(alpha), b, K, int(N), out, cap, ctypes.byref(cnt),
+                                         rf, rw, K, ctypes.byref(rc))
+    _check(st, "offset_attn_make_interp")
+    return [out[i] for i in range(cnt.value)], [(rf[i], rw[i]) for i in range(rc.value)]
+
+
+def offset_attn_fwd_interp(q, k, v, offsets, rungs, scale=None, out=None, lse=None):
+    """Offset attention with interpolated rungs ``rungs`` = [(floor, weight)]."""
+    B, H, Hkv, N, d = _check_qkv(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    offs = [int(x) for x in offsets]
+    arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
+    rf = (ctypes.c_int32 * max(1, len(rungs)))(*[int(a) for a, _ in rungs])
+    rw = (ctypes.c_float * max(1, len(rungs)))(*[float(w) for _, w in rungs])
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = L.lib().offset_attn_fwd_interp(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                                        B, H, Hkv, N, d, _strides(q, k, v, o), arr, len(offs), rf, rw, len(rungs),
+                                        scale, _stream(q.device))
+    _check(st, "offset_attn_fwd_interp")
+    return o, lse_t
+
+
 def offset_attn_fwd(q, k, v, offsets, scale=None, out=None, lse=None):
     """Offset attention; ``offsets`` a host list of ascending distances."""
     B, H, Hkv, N, d = _check_qkv(q, k, v)
@@ -337,7 +405,7 @@ class BlockSparsePlan:
 class OffsetPlan:
     """Pre-marshalled offset_attn_fwd call on fixed tensors (allocates nothing per call)."""
 
-    def __init__(self, q, k, v, offsets, scale=None):
+    def __init__(self, q, k, v, offsets, scale=None, rungs=None):
         B, H, Hkv, N, d = _check_qkv(q, k, v)
         self.device = q.device
         offs = [int(x) for x in offsets]
@@ -345,10 +413,18 @@ class OffsetPlan:
         self.o = torch.empty_like(q, memory_format=torch.contiguous_format)
         self.lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-        self._args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(self.o), _ptr(self.lse), B, H, Hkv,
-                      N, d, _strides(q, k, v, self.o), self._arr, len(offs), scale)
+        head = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(self.o), _ptr(self.lse), B, H, Hkv,
+                N, d, _strides(q, k, v, self.o), self._arr, len(offs))
         self._lib = L.lib()
+        if rungs is None:
+            self._fn, self._name = self._lib.offset_attn_fwd, "offset_attn_fwd"
+            self._args = head + (scale,)
+        else:
+            self._rf = (ctypes.c_int32 * max(1, len(rungs)))(*[int(a) for a, _ in rungs])
+            self._rw = (ctypes.c_float * max(1, len(rungs)))(*[float(w) for _, w in rungs])
+            self._fn, self._name = self._lib.offset_attn_fwd_interp, "offset_attn_fwd_interp"
+            self._args = head + (self._rf, self._rw, len(rungs), scale)
 
     def __call__(self):
-        _check(self._lib.offset_attn_fwd(*self._args, _stream(self.device)), "offset_attn_fwd")
+        _check(self._fn(*self._args, _stream(self.device)), self._name)
         return self.o, self.lse

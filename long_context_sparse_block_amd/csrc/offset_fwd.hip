@@ -71,6 +71,9 @@ struct OffArgs {
   int32_t nchunk; // workgroups per (batch, head)
   float scale_log2;
   int32_t offs[SA_MAX_OFFSETS];
+  int32_t nrung;  // interpolated rungs: key / value (1 - w) row[t - a] + w row[t - a - 1]
+  int32_t rfloor[SA_MAX_RUNGS];
+  float rw[SA_MAX_RUNGS];
 };
 
 template <bool BF16>
@@ -273,25 +276,36 @@ __global__ __launch_bounds__(256, D == 64 ? SA_OFF_WAVES64 : 2) void offset_mfma
   // Entry [dt][r] is d = 8 (4 (dt/2) + lane chunk) + 4 (dt%2) + r.
   sa::f32x4 acc[NDT];
   float l = 0.f;
+  // acc += pp.lo * row_a + pp.hi * row_b (bf16 pair weights), l += both weights
+  auto pv_pair = [&](uint32_t pp, const sa::u32x4 (&va)[NC], const sa::u32x4 (&vb)[NC]) {
+    l = sa::dot2_bf16(pp, lone, l);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        sa::f32x4& o = acc[2 * c + (x >> 1)];
+        o[2 * (x & 1)] = sa::dot2_bf16(pp, pair_lo(va[c][x], vb[c][x]), o[2 * (x & 1)]);
+        o[2 * (x & 1) + 1] = sa::dot2_bf16(pp, pair_hi(va[c][x], vb[c][x]), o[2 * (x & 1) + 1]);
+      }
+  };
   auto far_pv = [&](const float (&yf)[FC], float mu, sa::u32x4 (&vf)[FC][NC]) {
 #pragma unroll
     for (int n = 0; n < FC; ++n)
 #pragma unroll
       for (int c = 0; c < NC; ++c) sa::tie(vf[n][c]);
 #pragma unroll
-    for (int n = 0; n < FC; n += 2) {
-      const uint32_t pp = sa::pack_bf16x2(sa::fast_exp2(yf[n] - mu), sa::fast_exp2(yf[n + 1] - mu));
-      l = sa::dot2_bf16(pp, lone, l);
+    for (int n = 0; n < FC; n += 2)
+      pv_pair(sa::pack_bf16x2(sa::fast_exp2(yf[n] - mu), sa::fast_exp2(yf[n + 1] - mu)), vf[n], vf[n + 1]);
+  };
+  // rescale the running state to a new maximum mb > m
+  auto rescale = [&](float& m, float mb) {
+    const float alpha = sa::fast_exp2(m - mb);
+    l *= alpha;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const uint32_t va = vf[n][c][x], vb = vf[n + 1][c][x];
-          sa::f32x4& o = acc[2 * c + (x >> 1)];
-          o[2 * (x & 1)] = sa::dot2_bf16(pp, pair_lo(va, vb), o[2 * (x & 1)]);
-          o[2 * (x & 1) + 1] = sa::dot2_bf16(pp, pair_hi(va, vb), o[2 * (x & 1) + 1]);
-        }
-    }
+      for (int r = 0; r < 4; ++r) acc[dt][r] *= alpha;
+    m = mb;
   };
 
   if (has_near) {
@@ -426,17 +440,50 @@ __global__ __launch_bounds__(256, D == 64 ? SA_OFF_WAVES64 : 2) void offset_mfma
         float mb = yf[0];
 #pragma unroll
         for (int n = 1; n < FC; ++n) mb = fmaxf(mb, yf[n]);
-        if (mb > m) {  // per query (its 4 lanes agree): rescale the running state
-          const float alpha = sa::fast_exp2(m - mb);
-          l *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[dt][r] *= alpha;
-          m = mb;
-        }
+        if (mb > m) rescale(m, mb);  // per query (its 4 lanes agree)
         mu = m == -INFINITY ? 0.f : m;
       }
+    }
+    // Interpolated rungs, one online-softmax step each: rows t - a and
+    // t - a - 1 (both exist for t >= a + 1); the score is the same blend of
+    // the two rows' dot products, and the weight p splits into p (1 - w) and
+    // p w over the two value rows.
+    for (int r = 0; r < a.nrung; ++r) {
+      const int ra = a.rfloor[r];
+      const float rwt = a.rw[r];
+      const uint32_t s0 = (uint32_t)max(tqf - ra, 0), s1 = (uint32_t)max(tqf - ra - 1, 0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kf[0][c] = sa::gload16(Kh, s0 * krow + 16u * (4 * c + fj));
+        kf[1][c] = sa::gload16(Kh, s1 * krow + 16u * (4 * c + fj));
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        vf[0][c] = sa::gload16(Vh, s0 * vrow + 16u * (4 * c + fj));
+        vf[1][c] = sa::gload16(Vh, s1 * vrow + 16u * (4 * c + fj));
+      }
+      sa::vm_wait<2 * NC>();
+      float dot[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sa::tie(kf[n][c]);
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x = sa::dot2_bf16(qf[c][e], kf[n][c][e], x);
+        dot[n] = sa::quad_sum(x);
+      }
+      const float y = tqf >= ra + 1 ? ((1.f - rwt) * dot[0] + rwt * dot[1]) * c2 : -INFINITY;
+      if (y > m) rescale(m, y);
+      const float p = sa::fast_exp2(y - (m == -INFINITY ? 0.f : m));
+      sa::vm_wait<0>();
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sa::tie(vf[n][c]);
+      pv_pair(sa::pack_bf16x2(p * (1.f - rwt), p * rwt), vf[0], vf[1]);
     }
 
     l = sa::quad_sum(l);
@@ -520,6 +567,32 @@ __global__ __launch_bounds__(kThreads) void offset_fwd_kernel(OffArgs a) {
     }
   }
 
+  // interpolated rungs (valid for t >= a + 1), one rescale step each
+  for (int r = 0; r < a.nrung; ++r) {
+    const int ra = a.rfloor[r];
+    if (t < ra + 1) continue;
+    const float w = a.rw[r];
+    float k0[D], k1[D];
+    load_row<D, BF16>(K + (int64_t)(t - ra) * a.ks[2], k0);
+    load_row<D, BF16>(K + (int64_t)(t - ra - 1) * a.ks[2], k1);
+    float dot = 0.f;
+#pragma unroll
+    for (int x = 0; x < D; ++x) dot = fmaf(qf[x], fmaf(w, k1[x] - k0[x], k0[x]), dot);
+    const float y = dot * c2;
+    const float m_new = fmaxf(m, y);
+    const float alpha = sa::fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int x = 0; x < D; ++x) acc[x] *= alpha;
+    m = m_new;
+    const float p = sa::fast_exp2(y - m);
+    l += p;
+    load_row<D, BF16>(V + (int64_t)(t - ra) * a.vs[2], k0);
+    load_row<D, BF16>(V + (int64_t)(t - ra - 1) * a.vs[2], k1);
+#pragma unroll
+    for (int x = 0; x < D; ++x) acc[x] = fmaf(p, fmaf(w, k1[x] - k0[x], k0[x]), acc[x]);
+  }
+
   const float inv = l > 0.f ? 1.f / l : 0.f;
   T* orow = O + (int64_t)t * a.os[2];
   if constexpr (BF16) {
@@ -573,20 +646,80 @@ extern "C" sa_status offset_attn_make_table(int32_t W, double alpha, const int64
   return SA_OK;
 }
 
-extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
-                                     void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
-                                     int32_t N, int32_t d, const int64_t* strides,
-                                     const int32_t* offsets, int32_t num_offsets, float scale,
-                                     hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse || !offsets) return SA_ERR_NULL;
+extern "C" sa_status offset_attn_make_table_ratio(int32_t W, int64_t num, int64_t den, const int64_t* base,
+                                                  int32_t K, int32_t N, int32_t* table_out, int32_t capacity,
+                                                  int32_t* count_out) {
+  if (!table_out || !count_out || (K > 0 && !base)) return SA_ERR_NULL;
+  if (W < 0 || K < 0 || N < 1 || capacity < 0) return SA_ERR_INVALID;
+  const int64_t lim = (int64_t)1 << 31;
+  if (num < 0 || num >= lim || den < 1 || den >= lim) return SA_ERR_INVALID;
+  std::vector<int64_t> d;
+  for (int64_t x = 0; x <= W && x < N; ++x) d.push_back(x);
+  for (int j = 0; j < K; ++j) {
+    if (base[j] < 0 || base[j] >= lim) return SA_ERR_INVALID;
+    const int64_t x = (2 * num * base[j] + den) / (2 * den);  // floor(num f / den + 1/2), f >= 0
+    if (x < N) d.push_back(x);
+  }
+  std::sort(d.begin(), d.end());
+  d.erase(std::unique(d.begin(), d.end()), d.end());
+  if ((int64_t)d.size() > capacity) return SA_ERR_CAPACITY;
+  for (size_t j = 0; j < d.size(); ++j) table_out[j] = (int32_t)d[j];
+  *count_out = (int32_t)d.size();
+  return SA_OK;
+}
+
+extern "C" sa_status offset_attn_make_interp(int32_t W, double alpha, const int64_t* base, int32_t K, int32_t N,
+                                             int32_t* table_out, int32_t capacity, int32_t* count_out,
+                                             int32_t* rung_floor, float* rung_weight, int32_t rung_capacity,
+                                             int32_t* rung_count) {
+#pragma clang fp contract(off)
+  if (!table_out || !count_out || !rung_floor || !rung_weight || !rung_count || (K > 0 && !base))
+    return SA_ERR_NULL;
+  if (W < 0 || K < 0 || N < 1 || capacity < 0 || rung_capacity < 0 || !isfinite(alpha)) return SA_ERR_INVALID;
+  std::vector<int64_t> d;
+  std::vector<std::pair<int32_t, float>> rungs;
+  for (int64_t x = 0; x <= W && x < N; ++x) d.push_back(x);
+  for (int j = 0; j < K; ++j) {
+    if (base[j] < 0) return SA_ERR_INVALID;
+    const double x = alpha * (double)base[j];
+    if (x < 0.0) continue;  // negative distances reach no key
+    const double fl = floor(x);
+    if (x == fl) {
+      if (x < (double)N) d.push_back((int64_t)x);
+    } else if (fl + 1.0 <= (double)N - 1.0) {
+      rungs.push_back({(int32_t)fl, (float)(x - fl)});
+    }
+  }
+  std::sort(d.begin(), d.end());
+  d.erase(std::unique(d.begin(), d.end()), d.end());
+  if ((int64_t)d.size() > capacity || (int64_t)rungs.size() > rung_capacity) return SA_ERR_CAPACITY;
+  for (size_t j = 0; j < d.size(); ++j) table_out[j] = (int32_t)d[j];
+  for (size_t r = 0; r < rungs.size(); ++r) rung_floor[r] = rungs[r].first, rung_weight[r] = rungs[r].second;
+  *count_out = (int32_t)d.size();
+  *rung_count = (int32_t)rungs.size();
+  return SA_OK;
+}
+
+// Shared by both offset entry points (nrung = 0: integer distances only).
+static sa_status offset_run(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                            int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d, const int64_t* strides,
+                            const int32_t* offsets, int32_t num_offsets, const int32_t* rung_floor,
+                            const float* rung_weight, int32_t num_rungs, float scale, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || (num_offsets > 0 && !offsets)) return SA_ERR_NULL;
+  if (num_rungs > 0 && (!rung_floor || !rung_weight)) return SA_ERR_NULL;
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_INVALID;
   if (B < 1 || H < 1 || H_kv < 1 || N < 1 || d < 1) return SA_ERR_INVALID;
   if (H % H_kv != 0) return SA_ERR_INVALID;
   if (!isfinite(scale)) return SA_ERR_INVALID;
-  if (num_offsets < 1 || num_offsets > SA_MAX_OFFSETS) return SA_ERR_INVALID;
+  if (num_offsets < 0 || num_offsets > SA_MAX_OFFSETS) return SA_ERR_INVALID;
+  if (num_rungs < 0 || num_rungs > SA_MAX_RUNGS || num_offsets + num_rungs < 1) return SA_ERR_INVALID;
   for (int n = 0; n < num_offsets; ++n) {
     if (offsets[n] < 0 || offsets[n] >= N) return SA_ERR_INVALID;
     if (n > 0 && offsets[n] <= offsets[n - 1]) return SA_ERR_INVALID;
+  }
+  for (int r = 0; r < num_rungs; ++r) {
+    if (rung_floor[r] < 0 || (int64_t)rung_floor[r] + 1 > (int64_t)N - 1) return SA_ERR_INVALID;
+    if (!(rung_weight[r] >= 0.f && rung_weight[r] <= 1.f)) return SA_ERR_INVALID;
   }
   if (d != 64 && d != 128) return SA_ERR_UNSUPPORTED;
   const int64_t tiles = ((int64_t)N + kThreads - 1) / kThreads;
@@ -605,6 +738,8 @@ extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k
   a.B = B, a.H = H, a.H_kv = H_kv, a.N = N, a.noff = num_offsets;
   a.scale_log2 = scale * sa::kLog2e;
   for (int n = 0; n < num_offsets; ++n) a.offs[n] = offsets[n];
+  a.nrung = num_rungs;
+  for (int r = 0; r < num_rungs; ++r) a.rfloor[r] = rung_floor[r], a.rw[r] = rung_weight[r];
   a.nnear = 0;
   a.near_bits = 0;
   a.near64 = 0;
@@ -645,4 +780,25 @@ extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k
       hipLaunchKernelGGL((offset_fwd_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
   }
   return sa_host::check_launch("offset_fwd_kernel");
+}
+
+extern "C" sa_status offset_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                                     void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
+                                     int32_t N, int32_t d, const int64_t* strides,
+                                     const int32_t* offsets, int32_t num_offsets, float scale,
+                                     hipStream_t stream) {
+  if (!offsets) return SA_ERR_NULL;
+  if (num_offsets < 1) return SA_ERR_INVALID;
+  return offset_run(dtype, q, k, v, o, lse, B, H, H_kv, N, d, strides, offsets, num_offsets, nullptr,
+                    nullptr, 0, scale, stream);
+}
+
+extern "C" sa_status offset_attn_fwd_interp(int32_t dtype, const void* q, const void* k, const void* v,
+                                            void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
+                                            int32_t N, int32_t d, const int64_t* strides,
+                                            const int32_t* offsets, int32_t num_offsets,
+                                            const int32_t* rung_floor, const float* rung_weight,
+                                            int32_t num_rungs, float scale, hipStream_t stream) {
+  return offset_run(dtype, q, k, v, o, lse, B, H, H_kv, N, d, strides, offsets, num_offsets, rung_floor,
+                    rung_weight, num_rungs, scale, stream);
 }

@@ -64,6 +64,27 @@ OFFSET_WORKLOAD = dict(B=8, H=8, d=64, lengths=(2048, 8192), W=8, dtype=BF16,
                        alphas=tuple(1.0 + l / 15.0 for l in range(16)),
                        qkv_seed_base={2048: 1400, 8192: 1500})
 
+# Variants of the offset pattern ("Depth-Staggered Fibonacci Spacing for Sparse
+# Attention", Sec. 2), 16 calls each on the shape above at N = 2048:
+#  * stagger-ratio: Fibonacci base, alpha_l = 0.5 + l/15 held exactly (its rungs
+#    that land on a half round up);
+#  * power2-stagger: the power-of-2 control base with the same alpha ramp;
+#  * interp: continuous alpha_l = 0.5 + sigmoid(theta_l) with theta_l drawn
+#    N(0, 0.05^2) (a per-layer scalar that stays near its initialisation alpha
+#    = 1), so every rung is an interpolated gather.
+OFFSET_VARIANTS = {
+    "stagger-ratio": dict(base="fibonacci", ratios=tuple((15 + 2 * l, 30) for l in range(16)), qkv_seed_base=1600),
+    "power2-stagger": dict(base="power2", ratios=tuple((15 + 2 * l, 30) for l in range(16)), qkv_seed_base=1700),
+    "interp": dict(base="fibonacci", theta_seed=1800, theta_sd=0.05, qkv_seed_base=1800),
+}
+
+
+def interp_alphas(v, L=16):
+    """alpha_l = 0.5 + sigmoid(theta_l), theta_l ~ N(0, sd^2) from the variant's seed."""
+    g = np.random.default_rng(v["theta_seed"])
+    th = g.normal(0.0, v["theta_sd"], size=L)
+    return [0.5 + 1.0 / (1.0 + float(np.exp(-t))) for t in th]
+
 
 def mask_spec(w, **over):
     """Plain-dict mask description of a block workload (block units)."""

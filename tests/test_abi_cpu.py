@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from long_context_sparse_block_amd import _lib as L
@@ -168,3 +169,66 @@ def test_offset_table_capacity_error(lib):
     cnt = ctypes.c_int32()
     b = (ctypes.c_int64 * 1)(5)
     assert lib.offset_attn_make_table(3, 1.0, b, 1, 100, out, 2, ctypes.byref(cnt)) == L.SA_ERR_CAPACITY
+
+
+def _off_interp(lib, offsets, rungs, **kw):
+    fake = ctypes.c_void_p(1 << 20)
+    a = dict(dtype=L.SA_BF16, B=1, H=1, H_kv=1, N=64, d=64)
+    a.update(kw)
+    arr = (ctypes.c_int32 * max(1, len(offsets)))(*offsets)
+    rf = (ctypes.c_int32 * max(1, len(rungs)))(*[r[0] for r in rungs])
+    rw = (ctypes.c_float * max(1, len(rungs)))(*[r[1] for r in rungs])
+    return lib.offset_attn_fwd_interp(a["dtype"], fake, fake, fake, fake, fake, a["B"], a["H"], a["H_kv"],
+                                      a["N"], a["d"], None, arr, len(offsets), rf, rw, len(rungs), 0.125, None)
+
+
+@pytest.mark.parametrize("offsets,rungs,over,status", [
+    ([], [], {}, L.SA_ERR_INVALID),                       # no key at all
+    ([0], [(63, 0.5)], {}, L.SA_ERR_INVALID),             # a + 1 > N - 1
+    ([0], [(-1, 0.5)], {}, L.SA_ERR_INVALID),
+    ([0], [(3, 1.5)], {}, L.SA_ERR_INVALID),              # weight outside [0, 1]
+    ([0], [(3, -0.1)], {}, L.SA_ERR_INVALID),
+    ([0], [(3, float("nan"))], {}, L.SA_ERR_INVALID),
+    ([0], [(1, 0.5)] * (L.SA_MAX_RUNGS + 1), {}, L.SA_ERR_INVALID),
+    ([0, 0], [(1, 0.5)], {}, L.SA_ERR_INVALID),
+    ([0], [(1, 0.5)], dict(d=32), L.SA_ERR_UNSUPPORTED),
+])
+def test_offset_interp_host_errors(lib, offsets, rungs, over, status):
+    assert _off_interp(lib, offsets, rungs, **over) == status
+
+
+def test_offset_ratio_table_matches_oracle(lib):
+    fib15 = oo.fibonacci_base(1000)
+    for N in (64, 1024, 4096):
+        for l in range(16):
+            num, den = 15 + 2 * l, 30
+            assert api.offset_attn_make_table_ratio(8, num, den, fib15, N) == oo.offset_table_ratio(8, num, den, fib15, N)
+        for base in (oo.fibonacci_base(N), oo.power2_base(N)):
+            assert api.offset_attn_make_table_ratio(8, 7, 5, base, N) == oo.offset_table_ratio(8, 7, 5, base, N)
+    assert api.power2_base(1024) == oo.power2_base(1024)
+    b = (ctypes.c_int64 * 1)(5)
+    out = (ctypes.c_int32 * 8)()
+    cnt = ctypes.c_int32()
+    assert lib.offset_attn_make_table_ratio(3, 1, 0, b, 1, 100, out, 8, ctypes.byref(cnt)) == L.SA_ERR_INVALID
+    assert lib.offset_attn_make_table_ratio(3, -1, 2, b, 1, 100, out, 8, ctypes.byref(cnt)) == L.SA_ERR_INVALID
+    assert lib.offset_attn_make_table_ratio(3, 1, 1, b, 1, 100, out, 2, ctypes.byref(cnt)) == L.SA_ERR_CAPACITY
+
+
+def test_offset_interp_split_matches_oracle(lib):
+    for N in (64, 300, 2048):
+        for base in (oo.fibonacci_base(N), oo.power2_base(N)):
+            for alpha in (0.5, 0.73, 1.0, 1.0 + 1e-3, 1.37, 2.0, -1.0):
+                ints, rungs = api.offset_attn_make_interp(8, alpha, base, N)
+                oi, orr = oo.interp_split(8, alpha, base, N)
+                assert ints == oi
+                assert [a for a, _ in rungs] == [a for a, _ in orr]
+                assert [w for _, w in rungs] == [float(np.float32(w)) for _, w in orr]
+                if alpha == int(alpha) and alpha > 0:
+                    assert rungs == [] and ints == api.offset_attn_make_table(8, alpha, base, N)
+    b = (ctypes.c_int64 * 2)(3, 5)
+    out = (ctypes.c_int32 * 8)()
+    rf = (ctypes.c_int32 * 1)()
+    rw = (ctypes.c_float * 1)()
+    cnt, rc = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.offset_attn_make_interp(1, 1.5, b, 2, 100, out, 8, ctypes.byref(cnt), rf, rw, 1,
+                                       ctypes.byref(rc)) == L.SA_ERR_CAPACITY
