@@ -133,6 +133,8 @@ def interp_split(W, alpha, base, N):
     rungs = []
     for f in base:
         x = float(alpha) * float(f)
+        if x < 0:
+            continue  # a negative distance reaches no key
         a = math.floor(x)
         if x == a:
             ints.add(int(a))
