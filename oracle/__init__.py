@@ -26,8 +26,9 @@ Modules:
   literal     literal flags from byte content (gzip block sizes, mean threshold)
   block_mask  mask components, union, CSR, longest-first schedule
   attention   block-sparse attention: CSR-gather form and dense-masked form
-  offsets     offset table and token-level offset attention
+  offsets     offset table and token-level offset attention (and variants)
+  backward    gradients (dq, dk, dv) of both: dense-masked, CSR-gather, offsets
   tiny        pure-Python loop versions for tiny inputs (brute force)
 """
 
-from . import rng, literal, block_mask, attention, offsets, tiny  # noqa: F401
+from . import rng, literal, block_mask, attention, offsets, tiny, backward  # noqa: F401
