@@ -31,9 +31,12 @@ import numpy as np
 from . import attention as oa
 
 
-def _grads(qh, kh, vh, doh, allowed, scale):
+def _grads(qh, kh, vh, doh, allowed, scale, mags=False):
     """dq, dk, dv of one head over a boolean [Nq, Nk] mask (rows without keys
-    give zero)."""
+    give zero).  With ``mags`` also the term magnitudes of each entry, the same
+    sums with every factor replaced by its absolute value and D_t by
+    sum_x |dO_tx| |o_tx| added to |dp - D| (what a relative perturbation of the
+    weights p, of the products and of D can move the entry by)."""
     s = scale * (qh @ kh.T)
     s = np.where(allowed, s, -np.inf)
     p, _ = oa._softmax_rows(s)
@@ -44,7 +47,11 @@ def _grads(qh, kh, vh, doh, allowed, scale):
     ds = p * (dp - D[:, None])
     dq = scale * (ds @ kh)
     dk = scale * (ds.T @ qh)
-    return dq, dk, dv
+    if not mags:
+        return dq, dk, dv
+    Dabs = np.sum(np.abs(doh) * np.abs(o), axis=1)
+    dsm = p * (np.abs(dp - D[:, None]) + Dabs[:, None])
+    return (dq, dk, dv), (abs(scale) * (dsm @ np.abs(kh)), abs(scale) * (dsm.T @ np.abs(qh)), p.T @ np.abs(doh))
 
 
 def dense_masked_attention_bwd(q, k, v, do, block_masks, block, causal, scale,
@@ -70,17 +77,19 @@ def dense_masked_attention_bwd(q, k, v, do, block_masks, block, causal, scale,
 
 
 def csr_attention_bwd(q, k, v, do, row_ptr, col_idx, block, causal, scale,
-                      mask_batch_stride=0, mask_head_stride=0, heads=None):
+                      mask_batch_stride=0, mask_head_stride=0, heads=None, mags=False):
     """(dq, dk, dv) float64, one query block at a time over its key blocks.
 
     ``heads`` optionally restricts the work to (b, h) pairs (their
-    contributions only)."""
+    contributions only).  ``mags``: also return the term magnitudes (see
+    ``_grads``) as a second triple."""
     B, H, N, d = q.shape
     rep = H // k.shape[1]
     nb = N // block
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in pairs:
         g = b * mask_batch_stride + h * mask_head_stride
@@ -95,21 +104,28 @@ def csr_attention_bwd(q, k, v, do, row_ptr, col_idx, block, causal, scale,
             allowed = np.ones((block, keys.size), dtype=bool)
             if causal:
                 allowed = keys[None, :] <= qi[:, None]
-            a, c, e = _grads(q[b, h, qi], k[b, kh, keys], v[b, kh, keys], do[b, h, qi], allowed, scale)
+            r = _grads(q[b, h, qi], k[b, kh, keys], v[b, kh, keys], do[b, h, qi], allowed, scale, mags)
+            (a, c, e), m = (r, None) if not mags else r
             dq[b, h, qi] = a
             np.add.at(dk[b, kh], keys, c)
             np.add.at(dv[b, kh], keys, e)
-    return dq, dk, dv
+            if mags:
+                mq[b, h, qi] = m[0]
+                np.add.at(mk[b, kh], keys, m[1])
+                np.add.at(mv[b, kh], keys, m[2])
+    return ((dq, dk, dv), (mq, mk, mv)) if mags else (dq, dk, dv)
 
 
-def offset_attention_bwd(q, k, v, do, offsets, scale):
-    """(dq, dk, dv) float64 for keys {t - delta : delta in offsets, t - delta >= 0}."""
+def offset_attention_bwd(q, k, v, do, offsets, scale, mags=False):
+    """(dq, dk, dv) float64 for keys {t - delta : delta in offsets, t - delta >= 0}
+    (``mags``: also the term magnitudes, as for csr_attention_bwd)."""
     B, H, N, d = q.shape
     rep = H // k.shape[1]
     offs = list(offsets)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     t = np.arange(N)
     for b in range(B):
         for h in range(H):
@@ -126,6 +142,7 @@ def offset_attention_bwd(q, k, v, do, offsets, scale):
                 ok = src >= 0
                 o[ok] += p[ok, n][:, None] * v[b, kh, src[ok]]
             D = np.sum(do[b, h] * o, axis=1)
+            Dabs = np.sum(np.abs(do[b, h]) * np.abs(o), axis=1)
             for n, delta in enumerate(offs):
                 src = t - delta
                 ok = src >= 0
@@ -135,4 +152,9 @@ def offset_attention_bwd(q, k, v, do, offsets, scale):
                 dq[b, h, tt] += scale * ds[:, None] * k[b, kh, ss]
                 np.add.at(dk[b, kh], ss, scale * ds[:, None] * q[b, h, tt])
                 np.add.at(dv[b, kh], ss, p[ok, n][:, None] * do[b, h, tt])
-    return dq, dk, dv
+                if mags:
+                    dsm = p[ok, n] * (np.abs(dp - D[ok]) + Dabs[ok])
+                    mq[b, h, tt] += abs(scale) * dsm[:, None] * np.abs(k[b, kh, ss])
+                    np.add.at(mk[b, kh], ss, abs(scale) * dsm[:, None] * np.abs(q[b, h, tt]))
+                    np.add.at(mv[b, kh], ss, p[ok, n][:, None] * np.abs(do[b, h, tt]))
+    return ((dq, dk, dv), (mq, mk, mv)) if mags else (dq, dk, dv)

@@ -168,3 +168,24 @@ def test_offsets_bwd_special_cases():
     b = ob.csr_attention_bwd(q, k, v, do, *_csr(rows), 1, True, 0.5)
     for x, y in zip(a, b):
         np.testing.assert_allclose(x, y, atol=1e-12, rtol=0)
+
+
+def test_term_magnitudes_bound_the_gradients():
+    # |gradient entry| <= its term magnitude (triangle inequality), and with
+    # non-negative dO the value-gradient magnitudes are the value gradients
+    B, H, N, d, block = 1, 2, 24, 4, 4
+    q, k, v = _qkv(B, H, N, d, 21)
+    do = np.random.default_rng(22).standard_normal(q.shape)
+    nb = N // block
+    rows = [list(range(i + 1)) for i in range(nb)]
+    rp, ci = _csr(rows)
+    g, m = ob.csr_attention_bwd(q, k, v, do, rp, ci, block, True, 0.5, mags=True)
+    for x, y in zip(g, m):
+        assert np.all(np.abs(x) <= y + 1e-12)
+    g, m = ob.csr_attention_bwd(q, k, v, np.abs(do), rp, ci, block, True, 0.5, mags=True)
+    np.testing.assert_allclose(g[2], m[2], atol=1e-12)
+    g, m = ob.offset_attention_bwd(q, k, v, do, [0, 1, 5], 0.5, mags=True)
+    g2 = ob.offset_attention_bwd(q, k, v, do, [0, 1, 5], 0.5)
+    for x, y, z in zip(g, m, g2):
+        assert np.all(np.abs(x) <= y + 1e-12)
+        np.testing.assert_array_equal(x, z)
