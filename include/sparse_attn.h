@@ -1,14 +1,14 @@
 /*
  * sparse_attn.h -- C ABI of the MI355X (gfx950) sparse attention library.
  *
- * Three operations, all forward, all launched asynchronously on the caller's
- * HIP stream:
+ * Operations, all launched asynchronously on the caller's HIP stream:
  *
  *   sparse_attn_build_mask   block mask -> CSR key-block lists on the device
  *   sparse_attn_fwd          block-sparse attention over a CSR mask
  *   offset_attn_fwd          token-level attention over a table of distances
  *
- * and the offset_attn_fwd_interp variant, with host helpers
+ * with the offset_attn_fwd_interp variant, the backward passes
+ * (sparse_attn_mask_transpose, sparse_attn_bwd, offset_attn_bwd) and host helpers
  * (sparse_attn_mask_capacity, sparse_attn_literal_flags, offset_attn_make_table,
  * offset_attn_make_table_ratio, offset_attn_make_interp).
  *
@@ -302,6 +302,58 @@ sa_status offset_attn_fwd_interp(int32_t dtype, const void* q, const void* k, co
                                  const int64_t* strides, const int32_t* offsets, int32_t num_offsets,
                                  const int32_t* rung_floor, const float* rung_weight, int32_t num_rungs,
                                  float scale, hipStream_t stream);
+
+/*
+ * Backward pass (gradients of the loss L through o): given dO = dL/do, the
+ * gradients of masked softmax attention, from the saved lse,
+ *     D_t = <dO_t, o_t>,  p_ts = exp(scale <q_t, k_s> - lse_t),
+ *     dv_s = sum_t p_ts dO_t,  ds_ts = p_ts (<dO_t, v_s> - D_t),
+ *     dq_t = scale sum_s ds_ts k_s,  dk_s = scale sum_t ds_ts q_t
+ * over the allowed pairs (every page trains through the forward; the lse it
+ * returns is kept for this).  Grouped-query heads add into their K/V head.
+ */
+
+/*
+ * Transpose of a block mask: for every group g and key block j, the query
+ * blocks i whose CSR row lists j, ascending (rows must be ascending, as the
+ * builder writes them).  Entries outside [0, N_b) are ignored.
+ *   row_ptr, col_idx  DEVICE, as written by sparse_attn_build_mask
+ *   col_ptr           DEVICE int32 [G * N_b + 1] (written)
+ *   row_idx           DEVICE int32 [row_capacity] (written; row_capacity >=
+ *                     the number of mask entries keeps every entry)
+ */
+sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int64_t col_capacity, int32_t* col_ptr,
+                                     int32_t* row_idx, int64_t row_capacity, hipStream_t stream);
+
+/*
+ * Block-sparse attention backward over the mask used by sparse_attn_fwd
+ * (row_ptr / col_idx) and its transpose (col_ptr / row_idx from
+ * sparse_attn_mask_transpose).
+ *   q, k, v, o, lse  the forward's inputs and outputs; dout = dO [B, H, N, d]
+ *   dq [B, H, N, d], dk, dv [B, H_kv, N, d]  DEVICE, written (input dtype)
+ *   delta            DEVICE fp32 [B, H, N] workspace, written with D
+ *   strides          HOST int64 [8][3] for q, k, v, o, dout, dq, dk, dv
+ *                    (batch, head, sequence strides in elements) or NULL
+ * Other arguments, layouts, supported sizes and errors as for sparse_attn_fwd.
+ */
+sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
+                          int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d, int32_t block,
+                          const int64_t* strides, const int32_t* row_ptr, const int32_t* col_idx,
+                          int64_t col_capacity, const int32_t* col_ptr, const int32_t* row_idx,
+                          int64_t row_capacity, int32_t num_groups, int64_t mask_batch_stride,
+                          int64_t mask_head_stride, int32_t causal, float scale, hipStream_t stream);
+
+/*
+ * Offset attention backward over the table used by offset_attn_fwd.
+ * Tensors, delta and strides as for sparse_attn_bwd; offsets as for
+ * offset_attn_fwd.
+ */
+sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
+                          int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d, const int64_t* strides,
+                          const int32_t* offsets, int32_t num_offsets, float scale, hipStream_t stream);
 
 const char* sa_status_string(sa_status s);
 const char* sa_last_hip_error(void);

@@ -12,15 +12,18 @@ from .api import (  # noqa: F401
     head_group_spec,
     mask_preset,
     alpha_schedule,
+    offset_attn_bwd,
     offset_attn_fwd,
     offset_attn_fwd_interp,
     offset_attn_make_interp,
     offset_attn_make_table,
     offset_attn_make_table_ratio,
     power2_base,
+    sparse_attn_bwd,
     sparse_attn_build_mask,
     sparse_attn_check_mask_desc,
     sparse_attn_fwd,
     sparse_attn_literal_flags,
     sparse_attn_mask_capacity,
+    sparse_attn_mask_transpose,
 )

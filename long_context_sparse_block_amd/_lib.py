@@ -84,6 +84,12 @@ SIGNATURES = {
     "offset_attn_fwd_interp": (_i32, [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                       ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32),
                                       ctypes.POINTER(_f32), _i32, _f32, _p]),
+    "sparse_attn_mask_transpose": (_i32, [_i32, _i32, _p, _p, _i64, _p, _p, _i64, _p]),
+    "sparse_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               ctypes.POINTER(_i64), _p, _p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i32, _f32,
+                               _p]),
+    "offset_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                               ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, _f32, _p]),
     "sa_status_string": (ctypes.c_char_p, [_i32]),
     "sa_last_hip_error": (ctypes.c_char_p, []),
     "sa_version": (_i32, []),

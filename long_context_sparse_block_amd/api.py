@@ -204,7 +204,7 @@ def _strides(*ts):
     vals = []
     for t in ts:
         vals += [t.stride(0), t.stride(1), t.stride(2)]
-    return (ctypes.c_int64 * 12)(*vals)
+    return (ctypes.c_int64 * len(vals))(*vals)
 
 
 def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_stride=0,
@@ -225,6 +225,59 @@ def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_st
         scale, _stream(q.device))
     _check(st, "sparse_attn_fwd")
     return o, lse_t
+
+
+def sparse_attn_mask_transpose(mask):
+    """(col_ptr int32 [G*N_b+1], row_idx int32 [capacity]) device tensors: for
+    each key block the ascending query blocks whose row lists it."""
+    G, nb = mask.num_groups, mask.num_blocks
+    col_ptr = torch.empty(G * nb + 1, dtype=torch.int32, device=mask.row_ptr.device)
+    row_idx = torch.empty(mask.col_idx.numel(), dtype=torch.int32, device=mask.row_ptr.device)
+    st = L.lib().sparse_attn_mask_transpose(G, nb, _ptr(mask.row_ptr), _ptr(mask.col_idx), mask.col_idx.numel(),
+                                            _ptr(col_ptr), _ptr(row_idx), row_idx.numel(),
+                                            _stream(mask.row_ptr.device))
+    _check(st, "sparse_attn_mask_transpose")
+    return col_ptr, row_idx
+
+
+def _grad_outputs(q, k):
+    return (torch.empty_like(q, memory_format=torch.contiguous_format),
+            torch.empty_like(k, memory_format=torch.contiguous_format),
+            torch.empty_like(k, memory_format=torch.contiguous_format),
+            torch.empty(q.shape[:3], dtype=torch.float32, device=q.device))
+
+
+def sparse_attn_bwd(q, k, v, o, lse, dout, mask, transpose=None, scale=None, mask_batch_stride=0,
+                    mask_head_stride=0):
+    """Gradients (dq, dk, dv) of block-sparse attention; ``transpose`` is the
+    result of sparse_attn_mask_transpose(mask) (computed when omitted)."""
+    B, H, Hkv, N, d = _check_qkv(q, k, v)
+    block = N // mask.num_blocks
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    col_ptr, row_idx = transpose if transpose is not None else sparse_attn_mask_transpose(mask)
+    dq, dk, dv, delta = _grad_outputs(q, k)
+    st = L.lib().sparse_attn_bwd(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(delta), B, H, Hkv, N, d, block, _strides(q, k, v, o, dout, dq, dk, dv), _ptr(mask.row_ptr),
+        _ptr(mask.col_idx), mask.col_idx.numel(), _ptr(col_ptr), _ptr(row_idx), row_idx.numel(),
+        mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal), scale, _stream(q.device))
+    _check(st, "sparse_attn_bwd")
+    return dq, dk, dv
+
+
+def offset_attn_bwd(q, k, v, o, lse, dout, offsets, scale=None):
+    """Gradients (dq, dk, dv) of offset attention over ``offsets``."""
+    B, H, Hkv, N, d = _check_qkv(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    offs = [int(x) for x in offsets]
+    arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
+    dq, dk, dv, delta = _grad_outputs(q, k)
+    st = L.lib().offset_attn_bwd(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(delta), B, H, Hkv, N, d, _strides(q, k, v, o, dout, dq, dk, dv), arr, len(offs), scale,
+        _stream(q.device))
+    _check(st, "offset_attn_bwd")
+    return dq, dk, dv
 
 
 def sparse_attn_literal_flags(data, block_bytes, level=1):

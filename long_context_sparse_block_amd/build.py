@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIBDIR = os.path.join(HERE, "lib")
 LIBNAME = "libsparse_attn.so"
-SOURCES = ["host_common.hip", "mask_build.hip", "bsa_fwd.hip", "offset_fwd.hip", "literal_flags.cpp"]
+SOURCES = ["host_common.hip", "mask_build.hip", "bsa_fwd.hip", "offset_fwd.hip", "bwd.hip", "literal_flags.cpp"]
 ARCH = "gfx950"
 
 

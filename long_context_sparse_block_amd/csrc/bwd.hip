@@ -1,0 +1,786 @@
+// Gradients of block-sparse and offset attention (dq, dk, dv) from the saved
+// row log-sum-exp.  With P = exp(scale q k^T - lse) over the allowed pairs,
+// dO the upstream gradient and D_t = <dO_t, o_t>:
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//     dQ = scale dS K,   dK = scale dS^T Q
+// (masked pairs contribute nothing; grouped-query heads add into their K/V
+// head).  Kernels:
+//   * delta: D = rowsum(dO * O), fp32;
+//   * mask transpose: the CSR key-block lists -> per key block the ascending
+//     list of query blocks that list it (CSC), one wave per column;
+//   * block-sparse bf16: a dQ kernel over the CSR rows (one workgroup per
+//     query block, a wave per 32 queries, S^T = K Q^T so each lane owns a
+//     query) and a dK/dV kernel over the CSC columns (one workgroup per key
+//     block, a wave per 32 keys, S = Q K^T so each lane owns a key); all five
+//     products on v_mfma_f32_32x32x16_bf16, P and dS fed from the
+//     accumulators as B operands, the transposed A operands (K^T, Q^T, dO^T)
+//     by ds_read_b64_tr_b16 from LDS;
+//   * block-sparse fp32 and both offset kernels: one thread per row, plain
+//     fp32 arithmetic (exactness path; the offset kernels also take bf16).
+#include <math.h>
+
+#include <algorithm>
+
+#include "sa_device.h"
+#include "sa_host.h"
+
+namespace {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* lse;
+  float* delta;
+  int64_t st[8][3];  // q k v o dout dq dk dv: batch, head, sequence strides (elements)
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* col_ptr;
+  const int32_t* row_idx;
+  int64_t col_capacity, row_capacity;
+  int32_t B, H, H_kv, N, nb, G;
+  int64_t mbs, mhs;
+  int32_t causal;
+  float scale, c2;  // c2 = scale * log2(e)
+  int32_t noff;
+  int32_t offs[SA_MAX_OFFSETS];
+};
+
+enum { TQ = 0, TK = 1, TV = 2, TO = 3, TDO = 4, TDQ = 5, TDK = 6, TDV = 7 };
+
+inline sa_status allow_lds(const void* kern, int bytes) {
+  if (bytes <= 65536) return SA_OK;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return e == hipSuccess ? SA_OK : sa_host::record_hip_error(e, "hipFuncSetAttribute");
+}
+
+template <bool BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+  typedef uint16_t T;
+};
+template <>
+struct Elem<false> {
+  typedef float T;
+};
+
+// n consecutive elements -> floats (n a multiple of 8)
+template <int n, bool BF16>
+__device__ __forceinline__ void load_f(const typename Elem<BF16>::T* p, float* out) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int x = 0; x < n; x += 8) {
+      const sa::u32x4 w = *(const sa::u32x4*)(p + x);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[x + 2 * j] = sa::bf16_lo(w[j]), out[x + 2 * j + 1] = sa::bf16_hi(w[j]);
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < n; x += 4) {
+      const sa::f32x4 w = *(const sa::f32x4*)(p + x);
+      out[x] = w[0], out[x + 1] = w[1], out[x + 2] = w[2], out[x + 3] = w[3];
+    }
+  }
+}
+
+template <int n, bool BF16>
+__device__ __forceinline__ void store_f(typename Elem<BF16>::T* p, const float* in) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int x = 0; x < n; x += 8) {
+      sa::u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = sa::pack_bf16x2(in[x + 2 * j], in[x + 2 * j + 1]);
+      *(sa::u32x4*)(p + x) = w;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < n; x += 4) *(sa::f32x4*)(p + x) = sa::f32x4{in[x], in[x + 1], in[x + 2], in[x + 3]};
+  }
+}
+
+// lse * log2(e), with +inf for an empty row (its weights are then exp2(-inf) = 0)
+__device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * sa::kLog2e; }
+
+// ---------------------------------------------------------------- delta ----
+// D[b, h, t] = <dO_t, o_t>; D/8 lanes per row, 8 elements each.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
+  typedef typename Elem<BF16>::T T;
+  constexpr int LPR = D / 8;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;  // over B * H * N
+  const int part = threadIdx.x % LPR;
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const bool live = row < rows;
+  const int64_t rr = live ? row : 0;
+  const int64_t b = rr / ((int64_t)a.H * a.N), h = (rr / a.N) % a.H, t = rr % a.N;
+  const T* O = (const T*)a.o + b * a.st[TO][0] + h * a.st[TO][1] + t * a.st[TO][2] + 8 * part;
+  const T* G = (const T*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1] + t * a.st[TDO][2] + 8 * part;
+  float x[8], y[8];
+  load_f<8, BF16>(O, x);
+  load_f<8, BF16>(G, y);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s = fmaf(x[j], y[j], s);
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
+  if (live && part == 0) a.delta[rr] = s;
+}
+
+// ------------------------------------------------------- mask transpose ----
+struct TrArgs {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int32_t* col_ptr;
+  int32_t* row_idx;
+  int64_t col_capacity, row_capacity;
+  int32_t G, nb;
+};
+
+// Does row r (its entries ascending) list block j?
+__device__ __forceinline__ bool row_has(const TrArgs& t, int64_t r, int32_t j) {
+  int64_t lo = t.row_ptr[r], hi = t.row_ptr[r + 1];
+  lo = max((int64_t)0, min(lo, t.col_capacity));
+  hi = max(lo, min(hi, t.col_capacity));
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    const int32_t c = t.col_idx[mid];
+    if (c == j) return true;
+    if (c < j)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return false;
+}
+
+// One wave per column (g, j): FILL = false counts the rows listing j into
+// col_ptr[g * nb + j + 1]; FILL = true writes them ascending from col_ptr[g * nb + j].
+template <bool FILL>
+__global__ __launch_bounds__(256) void transpose_kernel(TrArgs t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= (int64_t)t.G * t.nb) return;
+  const int64_t g = col / t.nb;
+  const int32_t j = (int32_t)(col % t.nb);
+  int64_t pos = FILL ? t.col_ptr[col] : 0;
+  for (int32_t i0 = 0; i0 < t.nb; i0 += 64) {
+    const int32_t i = i0 + lane;
+    const bool hit = i < t.nb && row_has(t, g * t.nb + i, j);
+    const uint64_t m = __ballot(hit);
+    if (FILL && hit) {
+      const int64_t at = pos + __popcll(m & ((1ull << lane) - 1ull));
+      if (at < t.row_capacity) t.row_idx[at] = i;
+    }
+    pos += __popcll(m);
+  }
+  if (!FILL && lane == 0) t.col_ptr[col + 1] = (int32_t)pos;
+}
+
+// Inclusive scan of col_ptr[1 .. n] in place (col_ptr[0] = 0), one workgroup.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* p, int64_t n) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0, p[0] = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < n; base += 1024) {
+    const int64_t i = base + threadIdx.x;
+    int32_t v = i < n ? p[i + 1] : 0;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (i < n) p[i + 1] = part[threadIdx.x] + carry;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += part[1023];
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------- block-sparse helpers ----
+// CSR entry range of row (g, i), clamped to the capacity.
+__device__ __forceinline__ void row_range(const BwdArgs& a, int64_t g, int32_t i, int32_t& e0, int32_t& e1) {
+  const int64_t r = g * a.nb + i;
+  int64_t x = a.row_ptr[r], y = a.row_ptr[r + 1];
+  x = max((int64_t)0, min(x, a.col_capacity));
+  y = max(x, min(y, a.col_capacity));
+  e0 = sa::uniform((int32_t)x), e1 = sa::uniform((int32_t)y);
+}
+__device__ __forceinline__ void col_range(const BwdArgs& a, int64_t g, int32_t j, int32_t& e0, int32_t& e1) {
+  const int64_t c = g * a.nb + j;
+  int64_t x = a.col_ptr[c], y = a.col_ptr[c + 1];
+  x = max((int64_t)0, min(x, a.row_capacity));
+  y = max(x, min(y, a.row_capacity));
+  e0 = sa::uniform((int32_t)x), e1 = sa::uniform((int32_t)y);
+}
+
+// ----------------------------------------------------- block-sparse fp32 ---
+// dq: one thread per query of query block i (BLK threads), keys in 64-key tiles.
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK) void bsa_bwd_dq_f32(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float ksm[64][D];
+  __shared__ __attribute__((aligned(16))) float vsm[64][D];
+  const int tid = threadIdx.x;
+  const int32_t bh = blockIdx.x / a.nb, i = blockIdx.x % a.nb;
+  const int32_t b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
+  const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+  const int64_t t = (int64_t)i * BLK + tid;
+  const float* Q = (const float*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+  const float* K = (const float*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+  const float* V = (const float*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+  const float* G = (const float*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+  float* DQ = (float*)a.dq + b * a.st[TDQ][0] + h * a.st[TDQ][1];
+  float qv[D], gv[D], acc[D];
+  load_f<D, false>(Q + t * a.st[TQ][2], qv);
+  load_f<D, false>(G + t * a.st[TDO][2], gv);
+#pragma unroll
+  for (int x = 0; x < D; ++x) acc[x] = 0.f;
+  const int64_t row = ((int64_t)b * a.H + h) * a.N + t;
+  const float l2 = lse2_of(a.lse[row]), dd = a.delta[row];
+  int32_t e0, e1;
+  row_range(a, g, i, e0, e1);
+  for (int32_t e = e0; e < e1; ++e) {
+    const int32_t kb = a.col_idx[e];
+    if (kb < 0 || kb >= a.nb || (a.causal && kb > i)) continue;
+    for (int s0 = 0; s0 < BLK; s0 += 64) {
+      const int64_t key0 = (int64_t)kb * BLK + s0;
+      __syncthreads();
+      for (int u = tid; u < 64 * D / 4; u += BLK) {
+        const int key = u / (D / 4), c = u % (D / 4);
+        *(sa::f32x4*)&ksm[key][4 * c] = *(const sa::f32x4*)(K + (key0 + key) * a.st[TK][2] + 4 * c);
+        *(sa::f32x4*)&vsm[key][4 * c] = *(const sa::f32x4*)(V + (key0 + key) * a.st[TV][2] + 4 * c);
+      }
+      __syncthreads();
+      for (int kk = 0; kk < 64; ++kk) {
+        if (a.causal && key0 + kk > t) break;
+        float dot = 0.f, dp = 0.f;
+#pragma unroll
+        for (int x = 0; x < D; ++x) dot = fmaf(qv[x], ksm[kk][x], dot), dp = fmaf(gv[x], vsm[kk][x], dp);
+        const float p = exp2f(dot * a.c2 - l2);
+        const float ds = p * (dp - dd);
+#pragma unroll
+        for (int x = 0; x < D; ++x) acc[x] = fmaf(ds, ksm[kk][x], acc[x]);
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < D; ++x) acc[x] *= a.scale;
+  store_f<D, false>(DQ + t * a.st[TDQ][2], acc);
+}
+
+// dk, dv: one thread per key of key block j (BLK threads), over the q heads
+// of the K/V head and the query blocks that list j, queries in 32-row tiles.
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK) void bsa_bwd_dkdv_f32(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float qsm[32][D];
+  __shared__ __attribute__((aligned(16))) float gsm[32][D];
+  __shared__ float lsm[32], dsm[32];
+  const int tid = threadIdx.x;
+  const int32_t bk = blockIdx.x / a.nb, j = blockIdx.x % a.nb;
+  const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv, rep = a.H / a.H_kv;
+  const int64_t s = (int64_t)j * BLK + tid;
+  const float* K = (const float*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+  const float* V = (const float*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+  float kv[D], vv[D], dk[D], dv[D];
+  load_f<D, false>(K + s * a.st[TK][2], kv);
+  load_f<D, false>(V + s * a.st[TV][2], vv);
+#pragma unroll
+  for (int x = 0; x < D; ++x) dk[x] = dv[x] = 0.f;
+  for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+    const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+    const float* Q = (const float*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+    const float* G = (const float*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+    const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
+    int32_t e0, e1;
+    col_range(a, g, j, e0, e1);
+    for (int32_t e = e0; e < e1; ++e) {
+      const int32_t qb = a.row_idx[e];
+      if (qb < 0 || qb >= a.nb || (a.causal && qb < j)) continue;
+      for (int t0 = 0; t0 < BLK; t0 += 32) {
+        const int64_t q0 = (int64_t)qb * BLK + t0;
+        __syncthreads();
+        for (int u = tid; u < 32 * D / 4; u += BLK) {
+          const int r = u / (D / 4), c = u % (D / 4);
+          *(sa::f32x4*)&qsm[r][4 * c] = *(const sa::f32x4*)(Q + (q0 + r) * a.st[TQ][2] + 4 * c);
+          *(sa::f32x4*)&gsm[r][4 * c] = *(const sa::f32x4*)(G + (q0 + r) * a.st[TDO][2] + 4 * c);
+        }
+        if (tid < 32) lsm[tid] = lse2_of(a.lse[rowb + q0 + tid]), dsm[tid] = a.delta[rowb + q0 + tid];
+        __syncthreads();
+        for (int r = 0; r < 32; ++r) {
+          if (a.causal && q0 + r < s) continue;
+          float dot = 0.f, dp = 0.f;
+#pragma unroll
+          for (int x = 0; x < D; ++x) dot = fmaf(qsm[r][x], kv[x], dot), dp = fmaf(gsm[r][x], vv[x], dp);
+          const float p = exp2f(dot * a.c2 - lsm[r]);
+          const float ds = p * (dp - dsm[r]);
+#pragma unroll
+          for (int x = 0; x < D; ++x) dk[x] = fmaf(ds, qsm[r][x], dk[x]), dv[x] = fmaf(p, gsm[r][x], dv[x]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < D; ++x) dk[x] *= a.scale;
+  store_f<D, false>((float*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + s * a.st[TDK][2], dk);
+  store_f<D, false>((float*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + s * a.st[TDV][2], dv);
+}
+
+// ----------------------------------------------------- block-sparse bf16 ---
+// v_mfma_f32_32x32x16_bf16 layouts: A (32 x 16): lane l row l%32, k 8(l/32)..+8;
+// B (16 x 32): lane l column l%32, k 8(l/32)..+8; C: lane l column l%32,
+// rows 8(r/4) + 4(l/32) + r%4 for r < 16.  A product whose k index runs over
+// the rows of a C tile takes, for k-step s (16 rows), the C entries
+// r = 8s .. 8s+7 of the lane as its B operand; k slot 8(l/32) + e then stands
+// for row 16s + 8(e/4) + 4(l/32) + e%4, and the matching A operand is read
+// transposed from LDS with two ds_read_b64_tr_b16 (rows 16s + 4(l/32) + m and
+// 16s + 8 + 4(l/32) + m).
+
+// 16-byte chunk slot of a tile row in LDS (XOR of the row's low 3 bits)
+__device__ __forceinline__ int bswz(int c, int row) { return c ^ (row & 7); }
+
+template <int D>
+struct TileLds {
+  static constexpr int ROWB = 2 * D;
+  // A operand of rows [r0, r0 + 32), d-chunks 2u + l/32 (16 d per k-step u)
+  static __device__ __forceinline__ sa::u32x4 rows_a(const uint8_t* t, int r0, int u, int lane) {
+    const int row = r0 + (lane & 31);
+    return *(const sa::u32x4*)(t + row * ROWB + bswz(2 * u + (lane >> 5), row) * 16);
+  }
+  // transposed A operand: d rows 32 dt + l%32, k = tile rows 16 s + 8(e/4) + 4(l/32) + e%4
+  static __device__ __forceinline__ sa::u32x4 rows_tr(const uint8_t* t, int r0, int s, int dt, int lane) {
+    const int grp = lane >> 4, p = lane & 15, h = grp >> 1;
+    const int d0 = 32 * dt + 16 * (grp & 1) + 4 * (p & 3);  // first d of the lane's 8-byte word
+    const int ra = r0 + 16 * s + 4 * h + (p >> 2), rb = ra + 8;
+    const int ca = d0 >> 3, half = (d0 & 7) * 2;
+    const sa::u32x2 x = sa::lds_read_tr16(t + ra * ROWB + bswz(ca, ra) * 16 + half);
+    const sa::u32x2 y = sa::lds_read_tr16(t + rb * ROWB + bswz(ca, rb) * 16 + half);
+    return sa::u32x4{x[0], x[1], y[0], y[1]};
+  }
+};
+
+// Copy rows [r0, r0 + R) of a bf16 tensor (row stride rs elements) into a
+// swizzled LDS tile; nthr threads cooperate.
+template <int D>
+__device__ __forceinline__ void stage_rows(uint8_t* t, const uint16_t* src, int64_t r0, int64_t rs, int R,
+                                           int tid, int nthr) {
+  constexpr int CPR = D / 8;
+  for (int u = tid; u < R * CPR; u += nthr) {
+    const int r = u / CPR, c = u % CPR;
+    *(sa::u32x4*)(t + r * (2 * D) + bswz(c, r) * 16) = *(const sa::u32x4*)(src + (r0 + r) * rs + 8 * c);
+  }
+}
+
+// pack C entries 8s .. 8s+7 into a bf16 B operand
+__device__ __forceinline__ sa::u32x4 pack8(const float* x) {
+  return sa::u32x4{sa::pack_bf16x2(x[0], x[1]), sa::pack_bf16x2(x[2], x[3]), sa::pack_bf16x2(x[4], x[5]),
+                   sa::pack_bf16x2(x[6], x[7])};
+}
+
+// dq: one workgroup (BLK/32 waves) per query block, a wave per 32 queries.
+template <int D, int BLK>
+__global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
+  using L = TileLds<D>;
+  constexpr int NU = D / 16, NT = D / 32, NTH = 2 * BLK;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* ks = smem;
+  uint8_t* vs = smem + BLK * 2 * D;
+  const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
+  const int32_t bh = blockIdx.x / a.nb, i = blockIdx.x % a.nb;
+  const int32_t b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
+  const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+  const int64_t tq = (int64_t)i * BLK + 32 * w + (lane & 31);  // this lane's query (C column)
+  const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+  const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+  const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+  const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+  sa::u32x4 qb[NU], gb[NU];  // B operands: column = query, k = d 16u + 8(l/32) ..
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    qb[u] = *(const sa::u32x4*)(Q + tq * a.st[TQ][2] + 16 * u + 8 * hl);
+    gb[u] = *(const sa::u32x4*)(G + tq * a.st[TDO][2] + 16 * u + 8 * hl);
+  }
+  const int64_t row = ((int64_t)b * a.H + h) * a.N + tq;
+  const float l2 = lse2_of(a.lse[row]), dd = a.delta[row];
+  sa::f32x16 acc[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::f32x16{};
+  int32_t e0, e1;
+  row_range(a, g, i, e0, e1);
+  for (int32_t e = e0; e < e1; ++e) {
+    const int32_t kb = sa::uniform(a.col_idx[e]);
+    if (kb < 0 || kb >= a.nb || (a.causal && kb > i)) continue;
+    __syncthreads();
+    stage_rows<D>(ks, K, (int64_t)kb * BLK, a.st[TK][2], BLK, tid, NTH);
+    stage_rows<D>(vs, V, (int64_t)kb * BLK, a.st[TV][2], BLK, tid, NTH);
+    __syncthreads();
+#pragma unroll 1
+    for (int kt = 0; kt < BLK / 32; ++kt) {
+      // S^T and dP^T [32 keys x 32 queries]
+      sa::f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        s = sa::mfma32(L::rows_a(ks, 32 * kt, u, lane), qb[u], s);
+        dp = sa::mfma32(L::rows_a(vs, 32 * kt, u, lane), gb[u], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t key = (int64_t)kb * BLK + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float p = (a.causal && key > tq) ? 0.f : exp2f(s[r] * a.c2 - l2);
+        ds[r] = p * (dp[r] - dd);
+      }
+      // dQ^T [d x queries] += K^T [d x keys] dS^T [keys x queries]
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const sa::u32x4 bo = pack8(ds + 8 * st);
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::mfma32(L::rows_tr(ks, 32 * kt, st, dt, lane), bo, acc[dt]);
+      }
+    }
+  }
+  // C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's query
+  uint16_t* DQ = (uint16_t*)a.dq + b * a.st[TDQ][0] + h * a.st[TDQ][1] + tq * a.st[TDQ][2];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const sa::f32x16& x = acc[dt];
+      const int r = 4 * r4;
+      const sa::u32x2 wv = {sa::pack_bf16x2(x[r] * a.scale, x[r + 1] * a.scale),
+                            sa::pack_bf16x2(x[r + 2] * a.scale, x[r + 3] * a.scale)};
+      *(sa::u32x2*)(DQ + 32 * dt + 8 * r4 + 4 * hl) = wv;
+    }
+}
+
+// dk, dv: one workgroup (BLK/32 waves) per key block, a wave per 32 keys,
+// over the q heads of the K/V head and the query blocks that list the block.
+template <int D, int BLK>
+__global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
+  using L = TileLds<D>;
+  constexpr int NU = D / 16, NT = D / 32, NTH = 2 * BLK;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* qs = smem;
+  uint8_t* gs = smem + BLK * 2 * D;
+  float* ls = (float*)(smem + 2 * BLK * 2 * D);
+  float* dls = ls + BLK;
+  const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
+  const int32_t bk = blockIdx.x / a.nb, j = blockIdx.x % a.nb;
+  const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv, rep = a.H / a.H_kv;
+  const int64_t sk = (int64_t)j * BLK + 32 * w + (lane & 31);  // this lane's key (C column)
+  const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+  const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+  sa::u32x4 kb_[NU], vb_[NU];  // B operands: column = key, k = d
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    kb_[u] = *(const sa::u32x4*)(K + sk * a.st[TK][2] + 16 * u + 8 * hl);
+    vb_[u] = *(const sa::u32x4*)(V + sk * a.st[TV][2] + 16 * u + 8 * hl);
+  }
+  sa::f32x16 dk[NT], dv[NT];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) dk[dt] = sa::f32x16{}, dv[dt] = sa::f32x16{};
+  for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+    const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+    const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+    const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+    const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
+    int32_t e0, e1;
+    col_range(a, g, j, e0, e1);
+    for (int32_t e = e0; e < e1; ++e) {
+      const int32_t qb = sa::uniform(a.row_idx[e]);
+      if (qb < 0 || qb >= a.nb || (a.causal && qb < j)) continue;
+      __syncthreads();
+      stage_rows<D>(qs, Q, (int64_t)qb * BLK, a.st[TQ][2], BLK, tid, NTH);
+      stage_rows<D>(gs, G, (int64_t)qb * BLK, a.st[TDO][2], BLK, tid, NTH);
+      for (int r = tid; r < BLK; r += NTH) {
+        ls[r] = lse2_of(a.lse[rowb + (int64_t)qb * BLK + r]);
+        dls[r] = a.delta[rowb + (int64_t)qb * BLK + r];
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int qt = 0; qt < BLK / 32; ++qt) {
+        // S and dP [32 queries x 32 keys]
+        sa::f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
+          dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vb_[u], dp);
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
+          const sa::f32x4 l4 = *(const sa::f32x4*)(ls + q4);
+          const sa::f32x4 d4 = *(const sa::f32x4*)(dls + q4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * r4 + c;
+            const int64_t tq = (int64_t)qb * BLK + q4 + c;
+            p[r] = (a.causal && sk > tq) ? 0.f : exp2f(s[r] * a.c2 - l4[c]);
+            ds[r] = p[r] * (dp[r] - d4[c]);
+          }
+        }
+        // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) {
+            dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
+            dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
+          }
+        }
+      }
+    }
+  }
+  uint16_t* DK = (uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + sk * a.st[TDK][2];
+  uint16_t* DV = (uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + sk * a.st[TDV][2];
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const sa::f32x16& x = dk[dt];
+      const sa::f32x16& y = dv[dt];
+      const int r = 4 * r4;
+      *(sa::u32x2*)(DK + 32 * dt + 8 * r4 + 4 * hl) = sa::u32x2{
+          sa::pack_bf16x2(x[r] * a.scale, x[r + 1] * a.scale), sa::pack_bf16x2(x[r + 2] * a.scale, x[r + 3] * a.scale)};
+      *(sa::u32x2*)(DV + 32 * dt + 8 * r4 + 4 * hl) =
+          sa::u32x2{sa::pack_bf16x2(y[r], y[r + 1]), sa::pack_bf16x2(y[r + 2], y[r + 3])};
+    }
+}
+
+// --------------------------------------------------------------- offsets ---
+// dq: one thread per query; keys t - delta.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void off_bwd_dq(BwdArgs a) {
+  typedef typename Elem<BF16>::T T;
+  const int tiles = (a.N + 255) / 256;
+  const int32_t bh = blockIdx.x / tiles;
+  const int64_t t = (int64_t)(blockIdx.x % tiles) * 256 + threadIdx.x;
+  if (t >= a.N) return;
+  const int32_t b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
+  const T* K = (const T*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+  const T* V = (const T*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+  float qv[D], gv[D], acc[D];
+  load_f<D, BF16>((const T*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1] + t * a.st[TQ][2], qv);
+  load_f<D, BF16>((const T*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1] + t * a.st[TDO][2], gv);
+#pragma unroll
+  for (int x = 0; x < D; ++x) acc[x] = 0.f;
+  const int64_t row = ((int64_t)b * a.H + h) * a.N + t;
+  const float l2 = lse2_of(a.lse[row]), dd = a.delta[row];
+  for (int n = 0; n < a.noff && a.offs[n] <= t; ++n) {
+    const int64_t src = t - a.offs[n];
+    float kf[D], vf[D];
+    load_f<D, BF16>(K + src * a.st[TK][2], kf);
+    load_f<D, BF16>(V + src * a.st[TV][2], vf);
+    float dot = 0.f, dp = 0.f;
+#pragma unroll
+    for (int x = 0; x < D; ++x) dot = fmaf(qv[x], kf[x], dot), dp = fmaf(gv[x], vf[x], dp);
+    const float ds = exp2f(dot * a.c2 - l2) * (dp - dd);
+#pragma unroll
+    for (int x = 0; x < D; ++x) acc[x] = fmaf(ds, kf[x], acc[x]);
+  }
+#pragma unroll
+  for (int x = 0; x < D; ++x) acc[x] *= a.scale;
+  store_f<D, BF16>((T*)a.dq + b * a.st[TDQ][0] + h * a.st[TDQ][1] + t * a.st[TDQ][2], acc);
+}
+
+// dk, dv: one thread per key s of a K/V head; queries s + delta of every q head
+// of the group.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void off_bwd_dkdv(BwdArgs a) {
+  typedef typename Elem<BF16>::T T;
+  const int tiles = (a.N + 255) / 256;
+  const int32_t bk = blockIdx.x / tiles;
+  const int64_t s = (int64_t)(blockIdx.x % tiles) * 256 + threadIdx.x;
+  if (s >= a.N) return;
+  const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv, rep = a.H / a.H_kv;
+  float kv[D], vv[D], dk[D], dv[D];
+  load_f<D, BF16>((const T*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1] + s * a.st[TK][2], kv);
+  load_f<D, BF16>((const T*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1] + s * a.st[TV][2], vv);
+#pragma unroll
+  for (int x = 0; x < D; ++x) dk[x] = dv[x] = 0.f;
+  for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+    const T* Q = (const T*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+    const T* G = (const T*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+    const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
+    for (int n = 0; n < a.noff && s + a.offs[n] < a.N; ++n) {
+      const int64_t t = s + a.offs[n];
+      float qf[D], gf[D];
+      load_f<D, BF16>(Q + t * a.st[TQ][2], qf);
+      load_f<D, BF16>(G + t * a.st[TDO][2], gf);
+      float dot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int x = 0; x < D; ++x) dot = fmaf(qf[x], kv[x], dot), dp = fmaf(gf[x], vv[x], dp);
+      const float p = exp2f(dot * a.c2 - lse2_of(a.lse[rowb + t]));
+      const float ds = p * (dp - a.delta[rowb + t]);
+#pragma unroll
+      for (int x = 0; x < D; ++x) dk[x] = fmaf(ds, qf[x], dk[x]), dv[x] = fmaf(p, gf[x], dv[x]);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < D; ++x) dk[x] *= a.scale;
+  store_f<D, BF16>((T*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + s * a.st[TDK][2], dk);
+  store_f<D, BF16>((T*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + s * a.st[TDV][2], dv);
+}
+
+// ------------------------------------------------------------------ host ---
+template <typename F>
+sa_status launch(F kern, const BwdArgs& a, int64_t blocks, int threads, int lds, hipStream_t stream,
+                 const char* what) {
+  if (blocks <= 0) return SA_OK;
+  if (blocks > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
+  const sa_status ls = allow_lds((const void*)kern, lds);
+  if (ls != SA_OK) return ls;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), lds, stream, a);
+  return sa_host::check_launch(what);
+}
+
+// Shared argument checks of both backward entry points; fills a.
+sa_status common_args(BwdArgs& a, int32_t dtype, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta, int32_t B,
+                      int32_t H, int32_t H_kv, int32_t N, int32_t d, const int64_t* strides, float scale) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return SA_ERR_NULL;
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_INVALID;
+  if (B < 1 || H < 1 || H_kv < 1 || N < 1 || d < 1 || H % H_kv != 0) return SA_ERR_INVALID;
+  if (!isfinite(scale)) return SA_ERR_INVALID;
+  if (d != 64 && d != 128) return SA_ERR_UNSUPPORTED;
+  const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!sa_host::aligned16(p)) return SA_ERR_INVALID;
+  const int32_t heads[8] = {H, H_kv, H_kv, H, H, H, H_kv, H_kv};
+  const int align = dtype == SA_BF16 ? 8 : 4;
+  for (int t = 0; t < 8; ++t) {
+    int64_t sb, sh, ss;
+    if (!strides) {
+      ss = d, sh = (int64_t)N * d, sb = (int64_t)heads[t] * N * d;
+    } else {
+      sb = strides[3 * t], sh = strides[3 * t + 1], ss = strides[3 * t + 2];
+    }
+    if (ss < d || sh < 0 || sb < 0 || ss % align || sh % align || sb % align) return SA_ERR_INVALID;
+    a.st[t][0] = sb, a.st[t][1] = sh, a.st[t][2] = ss;
+  }
+  a.q = q, a.k = k, a.v = v, a.o = o, a.dout = dout, a.dq = dq, a.dk = dk, a.dv = dv;
+  a.lse = lse, a.delta = delta;
+  a.B = B, a.H = H, a.H_kv = H_kv, a.N = N;
+  a.scale = scale, a.c2 = scale * sa::kLog2e;
+  return SA_OK;
+}
+
+sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  const int64_t blocks = (rows * (d / 8) + 255) / 256;
+  if (dtype == SA_BF16)
+    return d == 64 ? launch(delta_kernel<64, true>, a, blocks, 256, 0, stream, "delta_kernel")
+                   : launch(delta_kernel<128, true>, a, blocks, 256, 0, stream, "delta_kernel");
+  return d == 64 ? launch(delta_kernel<64, false>, a, blocks, 256, 0, stream, "delta_kernel")
+                 : launch(delta_kernel<128, false>, a, blocks, 256, 0, stream, "delta_kernel");
+}
+
+template <int D, int BLK>
+sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  const int64_t nq = (int64_t)a.B * a.H * a.nb, nk = (int64_t)a.B * a.H_kv * a.nb;
+  sa_status st;
+  if (bf16) {
+    st = launch(bsa_bwd_dq_bf16<D, BLK>, a, nq, 2 * BLK, 2 * BLK * 2 * D, stream, "bsa_bwd_dq_bf16");
+    if (st != SA_OK) return st;
+    return launch(bsa_bwd_dkdv_bf16<D, BLK>, a, nk, 2 * BLK, 2 * BLK * 2 * D + 2 * BLK * 4, stream,
+                  "bsa_bwd_dkdv_bf16");
+  }
+  st = launch(bsa_bwd_dq_f32<D, BLK>, a, nq, BLK, 0, stream, "bsa_bwd_dq_f32");
+  if (st != SA_OK) return st;
+  return launch(bsa_bwd_dkdv_f32<D, BLK>, a, nk, BLK, 0, stream, "bsa_bwd_dkdv_f32");
+}
+
+}  // namespace
+
+extern "C" sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, const int32_t* row_ptr,
+                                                const int32_t* col_idx, int64_t col_capacity, int32_t* col_ptr,
+                                                int32_t* row_idx, int64_t row_capacity, hipStream_t stream) {
+  if (!row_ptr || !col_idx || !col_ptr || !row_idx) return SA_ERR_NULL;
+  if (num_groups < 1 || num_blocks < 1 || num_blocks > SA_MAX_BLOCKS || col_capacity < 0 || row_capacity < 0)
+    return SA_ERR_INVALID;
+  const int64_t cols = (int64_t)num_groups * num_blocks;
+  if (cols >= 0x7fffffffll) return SA_ERR_UNSUPPORTED;
+  TrArgs t = {row_ptr, col_idx, col_ptr, row_idx, col_capacity, row_capacity, num_groups, num_blocks};
+  const unsigned blocks = (unsigned)((cols + 3) / 4);
+  hipLaunchKernelGGL((transpose_kernel<false>), dim3(blocks), dim3(256), 0, stream, t);
+  sa_status st = sa_host::check_launch("transpose_kernel<count>");
+  if (st != SA_OK) return st;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, col_ptr, cols);
+  st = sa_host::check_launch("scan_kernel");
+  if (st != SA_OK) return st;
+  hipLaunchKernelGGL((transpose_kernel<true>), dim3(blocks), dim3(256), 0, stream, t);
+  return sa_host::check_launch("transpose_kernel<fill>");
+}
+
+extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                     float* delta, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                     int32_t block, const int64_t* strides, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int64_t col_capacity, const int32_t* col_ptr,
+                                     const int32_t* row_idx, int64_t row_capacity, int32_t num_groups,
+                                     int64_t mask_batch_stride, int64_t mask_head_stride, int32_t causal,
+                                     float scale, hipStream_t stream) {
+  BwdArgs a = {};
+  if (!row_ptr || !col_idx || !col_ptr || !row_idx) return SA_ERR_NULL;
+  sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, strides, scale);
+  if (st != SA_OK) return st;
+  if (block < 1 || causal < 0 || causal > 1 || col_capacity < 0 || row_capacity < 0) return SA_ERR_INVALID;
+  if (num_groups < 1 || mask_batch_stride < 0 || mask_head_stride < 0) return SA_ERR_INVALID;
+  if ((int64_t)(B - 1) * mask_batch_stride + (int64_t)(H - 1) * mask_head_stride >= num_groups)
+    return SA_ERR_INVALID;
+  if (N % block != 0) return SA_ERR_INVALID;
+  if (block != 64 && block != 128) return SA_ERR_UNSUPPORTED;
+  a.row_ptr = row_ptr, a.col_idx = col_idx, a.col_ptr = col_ptr, a.row_idx = row_idx;
+  a.col_capacity = col_capacity, a.row_capacity = row_capacity;
+  a.nb = N / block, a.G = num_groups, a.mbs = mask_batch_stride, a.mhs = mask_head_stride, a.causal = causal;
+  st = launch_delta(a, dtype, d, stream);
+  if (st != SA_OK) return st;
+  const bool bf = dtype == SA_BF16;
+  if (d == 64) return block == 64 ? launch_bsa_bwd<64, 64>(a, bf, stream) : launch_bsa_bwd<64, 128>(a, bf, stream);
+  return block == 64 ? launch_bsa_bwd<128, 64>(a, bf, stream) : launch_bsa_bwd<128, 128>(a, bf, stream);
+}
+
+extern "C" sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                     float* delta, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                     const int64_t* strides, const int32_t* offsets, int32_t num_offsets,
+                                     float scale, hipStream_t stream) {
+  BwdArgs a = {};
+  if (!offsets) return SA_ERR_NULL;
+  sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, strides, scale);
+  if (st != SA_OK) return st;
+  if (num_offsets < 1 || num_offsets > SA_MAX_OFFSETS) return SA_ERR_INVALID;
+  for (int n = 0; n < num_offsets; ++n) {
+    if (offsets[n] < 0 || offsets[n] >= N) return SA_ERR_INVALID;
+    if (n > 0 && offsets[n] <= offsets[n - 1]) return SA_ERR_INVALID;
+  }
+  a.noff = num_offsets;
+  for (int n = 0; n < num_offsets; ++n) a.offs[n] = offsets[n];
+  st = launch_delta(a, dtype, d, stream);
+  if (st != SA_OK) return st;
+  const int64_t tiles = ((int64_t)N + 255) / 256;
+  const int64_t nq = (int64_t)B * H * tiles, nk = (int64_t)B * H_kv * tiles;
+  if (dtype == SA_BF16) {
+    st = d == 64 ? launch(off_bwd_dq<64, true>, a, nq, 256, 0, stream, "off_bwd_dq")
+                 : launch(off_bwd_dq<128, true>, a, nq, 256, 0, stream, "off_bwd_dq");
+    if (st != SA_OK) return st;
+    return d == 64 ? launch(off_bwd_dkdv<64, true>, a, nk, 256, 0, stream, "off_bwd_dkdv")
+                   : launch(off_bwd_dkdv<128, true>, a, nk, 256, 0, stream, "off_bwd_dkdv");
+  }
+  st = d == 64 ? launch(off_bwd_dq<64, false>, a, nq, 256, 0, stream, "off_bwd_dq")
+               : launch(off_bwd_dq<128, false>, a, nq, 256, 0, stream, "off_bwd_dq");
+  if (st != SA_OK) return st;
+  return d == 64 ? launch(off_bwd_dkdv<64, false>, a, nk, 256, 0, stream, "off_bwd_dkdv")
+                 : launch(off_bwd_dkdv<128, false>, a, nk, 256, 0, stream, "off_bwd_dkdv");
+}

@@ -1,0 +1,208 @@
+"""GPU backward passes vs the fp64 oracle gradients: the block-mask transpose
+(bit-exact), block-sparse dq / dk / dv (fp32 and bf16, GQA, per-head mask
+groups, strided layouts, reduced and full-size workloads) and offset dq / dk /
+dv.
+
+Bars for gradients (derived from the arithmetic).  Each gradient entry is a
+sum of terms; M is the same sum with every factor taken in absolute value
+(oracle term magnitudes, D_t counted as sum |dO_tx| |o_tx|).  bf16 path: the
+forward's lse is accurate to 2^-9 (its normaliser sums bf16-rounded weights),
+so every recomputed weight p is off by up to 2^-9 relative; P and dS enter the
+MFMAs rounded to bf16 (2^-9); D_t is formed from the stored bf16 o (2^-9 of
+its magnitude); the output is rounded to bf16 (2^-9 of the entry).  Hence
+|g - ref| <= 2^-7 M + 2^-8 |ref| per entry, and the mean error stays below
+2^-8 mean(M).  fp32 path: |g - ref| <= 1e-5 (M + |ref|) + 1e-7 (fp32 rounding
+of the exp2 argument, about 1e-6 of every weight)."""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_block_amd import api
+from long_context_sparse_block_amd import workloads as wl
+from oracle import backward as ob
+from oracle import block_mask as bm
+from oracle import offsets as oo
+from tests.gpu_util import announce, f64, require_gpu, workload_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def compare_grads(gpu, ref, mag, dtype, what):
+    g = f64(gpu)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    diff = np.abs(g - ref)
+    if dtype == torch.bfloat16:
+        lim = 2.0 ** -7 * mag + 2.0 ** -8 * np.abs(ref) + 1e-6
+        assert diff.mean() <= 2.0 ** -8 * mag.mean() + 1e-7, f"{what}: mean-abs {diff.mean():.3e} vs mean M {mag.mean():.3e}"
+    else:
+        lim = 1e-5 * (mag + np.abs(ref)) + 1e-7
+    bad = int(np.argmax(diff - lim))
+    assert np.all(diff <= lim), (f"{what}: |err| {diff.flat[bad]:.3e} > bar {lim.flat[bad]:.3e} "
+                                 f"(|ref| {abs(ref.flat[bad]):.3e}, index {np.unravel_index(bad, ref.shape)})")
+    return float(np.max(diff / lim))
+
+
+def _dout(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype)
+
+
+def _bsa_case(spec, B, H, Hkv, N, d, dtype, seed, scale=None, heads=None, layout=None):
+    block = N // spec["num_blocks"]
+    q, k, v = wl.make_qkv(B, H, N, d, dtype, seed, H_kv=Hkv)
+    do = _dout(q.shape, dtype, seed + 1)
+    if layout == "bnhd":  # [B, N, H, d] storage viewed as [B, H, N, d]
+        q, k, v, do = [t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v, do)]
+    qd, kd, vd, dod = [t.cuda() for t in (q, k, v, do)]
+    mask = api.sparse_attn_build_mask(spec)
+    mbs, mhs = spec["mask_batch_stride"], spec["mask_head_stride"]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, scale, mbs, mhs)
+    dq, dk, dv = api.sparse_attn_bwd(qd, kd, vd, o, lse, dod, mask, None, scale, mbs, mhs)
+    torch.cuda.synchronize()
+    rp, ci, _ = bm.build(spec)
+    ref = ob.csr_attention_bwd(f64(q), f64(k), f64(v), f64(do), rp, ci, block, spec["causal"], scale, mbs, mhs,
+                               heads=heads, mags=True)
+    return (dq, dk, dv), ref
+
+
+def _check_all(got, ref, dtype, what, heads=None):
+    (gq, gk, gv), (mq, mk, mv) = ref
+    for n, gt, rf, mg in zip(("dq", "dk", "dv"), got, (gq, gk, gv), (mq, mk, mv)):
+        if heads is not None:
+            gt = torch.stack([gt[b, h] for b, h in heads])
+            rf = np.stack([rf[b, h] for b, h in heads])
+            mg = np.stack([mg[b, h] for b, h in heads])
+        compare_grads(gt, rf, mg, dtype, f"{what} {n}")
+
+
+def _specs():
+    out = []
+    for name in ("compression-guided", "bigbird", "long-context", "gzip-head-groups"):
+        w = wl.BLOCK_WORKLOADS[name]
+        out.append((name, workload_spec(dict(w, B=min(w["B"], 2)))))
+    R = random.Random(3)
+    for s in range(4):
+        nb = R.randint(1, 40)
+        causal = s % 2 == 0
+        out.append((f"random{s}", dict(num_blocks=nb, num_groups=3, causal=causal, win_before=R.randint(0, 3),
+                                       win_after=0 if causal else 1, win_clamp=True,
+                                       global_blocks=[0] if nb > 1 else [], num_random=2, random_blocks=None,
+                                       literal_mode="pair", literal_flags=None, literal_p=0.3, seed=s,
+                                       mask_batch_stride=1, mask_head_stride=0)))
+    return out
+
+
+def test_mask_transpose_bitexact():
+    require_gpu()
+    for name, spec in _specs():
+        announce(f"[bwd] transpose {name}")
+        mask = api.sparse_attn_build_mask(spec)
+        col_ptr, row_idx = api.sparse_attn_mask_transpose(mask)
+        torch.cuda.synchronize()
+        m = bm.block_mask(spec)
+        cp_ref, ri_ref = bm.to_csr(np.transpose(m, (0, 2, 1)))
+        assert np.array_equal(col_ptr.cpu().numpy(), cp_ref), name
+        n = int(cp_ref[-1])
+        assert np.array_equal(row_idx[:n].cpu().numpy(), ri_ref), name
+
+
+def test_bsa_bwd_fp32_tiny_workload():
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS["tiny-fp32"]
+    announce("[bwd] bsa fp32 tiny workload")
+    got, ref = _bsa_case(wl.mask_spec(w), w["B"], w["H"], w["H"], w["N"], w["d"], torch.float32, w["qkv_seed"])
+    _check_all(got, ref, torch.float32, "tiny")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_bsa_bwd_gqa_head_groups(dtype, d, block):
+    """GQA (4 q heads on 2 K/V heads) with one mask group per q head, causal
+    and non-causal, rows whose only entries lie in the future."""
+    require_gpu()
+    N = 8 * block
+    for causal in (True, False):
+        spec = dict(num_blocks=N // block, num_groups=4, causal=causal, win_before=1, win_after=0 if causal else 1,
+                    win_clamp=True, global_blocks=[0], num_random=2, random_blocks=None, literal_mode="anyq",
+                    literal_flags=None, literal_p=0.3, seed=11, mask_batch_stride=0, mask_head_stride=1)
+        announce(f"[bwd] bsa gqa {dtype} d={d} block={block} causal={causal}")
+        got, ref = _bsa_case(spec, 2, 4, 2, N, d, dtype, 40 + d + block)
+        _check_all(got, ref, dtype, f"gqa d={d} b={block} causal={causal}")
+
+
+@pytest.mark.parametrize("name,B,H", [("compression-guided", 2, 2), ("bigbird", 1, 3), ("long-context", 1, 2),
+                                      ("gzip-head-groups", 1, 12)])
+def test_bsa_bwd_bf16_reduced_workloads(name, B, H):
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS[name]
+    N = w["N"] if name != "long-context" else 8192
+    w = dict(w, B=B, H=H, N=N)
+    spec = workload_spec(w)
+    announce(f"[bwd] bsa {name} B={B} H={H} N={N}")
+    got, ref = _bsa_case(spec, B, H, H, N, w["d"], torch.bfloat16, w["qkv_seed"])
+    _check_all(got, ref, torch.bfloat16, name)
+
+
+def test_bsa_bwd_bf16_strided_negative_scale():
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS["bigbird"]
+    spec = workload_spec(dict(w, B=1))
+    announce("[bwd] bsa strided [B,N,H,d], scale -0.1")
+    got, ref = _bsa_case(spec, 1, 4, 4, w["N"], 64, torch.bfloat16, 77, scale=-0.1, layout="bnhd")
+    _check_all(got, ref, torch.bfloat16, "strided")
+
+
+def test_bsa_bwd_bf16_full_size_sampled_heads():
+    """The headline workload at full size; whole (batch, head) slices checked."""
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS["compression-guided"]
+    heads = [(0, 0), (w["B"] - 1, w["H"] - 1), (2, 5)]
+    announce(f"[bwd] bsa compression-guided full {w['B']}x{w['H']}x{w['N']}")
+    got, ref = _bsa_case(workload_spec(w), w["B"], w["H"], w["H"], w["N"], w["d"], torch.bfloat16, w["qkv_seed"],
+                         heads=heads)
+    _check_all(got, ref, torch.bfloat16, "full", heads=heads)
+
+
+def _off_case(offs, B, H, Hkv, N, d, dtype, seed, scale):
+    q, k, v = wl.make_qkv(B, H, N, d, dtype, seed, H_kv=Hkv)
+    do = _dout(q.shape, dtype, seed + 1)
+    qd, kd, vd, dod = [t.cuda() for t in (q, k, v, do)]
+    o, lse = api.offset_attn_fwd(qd, kd, vd, offs, scale)
+    got = api.offset_attn_bwd(qd, kd, vd, o, lse, dod, offs, scale)
+    torch.cuda.synchronize()
+    ref = ob.offset_attention_bwd(f64(q), f64(k), f64(v), f64(do), offs, scale, mags=True)
+    return got, ref
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_offset_bwd_ragged_gqa(dtype, d):
+    require_gpu()
+    for N, Hkv in ((1, 2), (63, 1), (300, 2), (1000, 1)):
+        offs = oo.offset_table(5, 1.3, oo.fibonacci_base(N), N)
+        announce(f"[bwd] offsets N={N} d={d} {dtype} H_kv={Hkv}")
+        got, ref = _off_case(offs, 2, 2, Hkv, N, d, dtype, 600 + N, 0.2)
+        _check_all(got, ref, dtype, f"offsets N={N}")
+
+
+def test_offset_bwd_no_self_distance():
+    """Table without distance 0: the first queries have no key (lse = -inf)."""
+    require_gpu()
+    got, ref = _off_case([3, 7, 20], 1, 2, 2, 200, 64, torch.bfloat16, 650, 0.3)
+    _check_all(got, ref, torch.bfloat16, "no self")
+
+
+def test_offset_bwd_workload_reduced_batch():
+    require_gpu()
+    ow = wl.OFFSET_WORKLOAD
+    for N in ow["lengths"]:
+        offs = oo.offset_table(ow["W"], ow["alphas"][7], oo.fibonacci_base(N), N)
+        announce(f"[bwd] offsets workload N={N} B=1 H=2")
+        got, ref = _off_case(offs, 1, 2, 2, N, ow["d"], torch.bfloat16, ow["qkv_seed_base"][N] + 7,
+                             1 / math.sqrt(ow["d"]))
+        _check_all(got, ref, torch.bfloat16, f"offsets workload N={N}")
