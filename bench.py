@@ -147,6 +147,49 @@ def block_workload(name, steps, warmup, kernel_iters):
                 mask_ms=mask_ms, wall_s=wall, nnz=nnz, plan=plan, q=q, k=k, v=v, flags_ms=flags_ms)
 
 
+def block_backward(res, reps):
+    """sparse_attn_bwd on a block workload's forward outputs (seeded dO)."""
+    plan = res["plan"]
+    plan()
+    g = torch.Generator().manual_seed(4242)
+    dout = torch.randn(plan.q.shape, generator=g).to(plan.q.dtype).cuda()
+    bp = api.BlockSparseBwdPlan(plan, dout)
+    bp()
+    torch.cuda.synchronize()
+    bwd_ms = time_events(bp, reps)
+    tr_ms = time_events(bp.transpose, reps)
+    # five products per tile (dV, dP, dS-based dQ and dK, and S recomputed):
+    # 2.5x the forward's two, as algorithmic FLOPs
+    flops = 2.5 * res["flops"]
+    return dict(bwd_ms=bwd_ms, transpose_ms=tr_ms, flops=flops, tflops=flops / (bwd_ms * 1e-3) / 1e12)
+
+
+def backward_line(name, r):
+    return {"workload": f"{name} backward (dq, dk, dv; mask transpose timed apart)",
+            "value": round(r["tflops"], 3), "unit": "TFLOP/s", "bwd_ms": round(r["bwd_ms"], 5),
+            "mask_transpose_ms": round(r["transpose_ms"], 5), "alg_gflop": round(r["flops"] / 1e9, 3),
+            "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 3), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_BF16_TFLOPS, 4)}}
+
+
+def offset_backward(N, reps):
+    ow = wl.OFFSET_WORKLOAD
+    B, H, d = ow["B"], ow["H"], ow["d"]
+    offs = api.offset_attn_make_table(ow["W"], ow["alphas"][7], api.fibonacci_base(N), N)
+    q, k, v = [t.cuda() for t in wl.make_qkv(B, H, N, d, torch.bfloat16, ow["qkv_seed_base"][N] + 7)]
+    fp = api.OffsetPlan(q, k, v, offs)
+    fp()
+    g = torch.Generator().manual_seed(4343)
+    dout = torch.randn(q.shape, generator=g).to(q.dtype).cuda()
+    bp = api.OffsetBwdPlan(fp, offs, dout)
+    bp()
+    torch.cuda.synchronize()
+    ms = time_events(bp, reps)
+    # q, k, v, o, dO read once, dq, dk, dv written once, lse read, D written and read
+    byt = B * H * N * (8 * d * 2 + 12)
+    return dict(ms=ms, bytes=byt, gbs=byt / (ms * 1e-3) / 1e9)
+
+
 def offset_workload(N, reps, warmup):
     ow = wl.OFFSET_WORKLOAD
     B, H, d = ow["B"], ow["H"], ow["d"]
@@ -313,8 +356,12 @@ def main():
                 line["gzip_flags_host_ms"] = round(r["flags_ms"], 4)
                 line["literal_fraction"] = round(float(np.mean(r["spec"]["literal_flags"])), 4)
             sec.append(line)
+            if name == "long-context":
+                sec.append(backward_line(name, block_backward(r, reps=5)))
             del r
             torch.cuda.empty_cache()
+        sec.append(backward_line(HEADLINE, block_backward(head, reps=50)))
+        torch.cuda.empty_cache()
         for N in wl.OFFSET_WORKLOAD["lengths"]:
             r = offset_workload(N, reps=5, warmup=1)
             sec.append({"workload": f"fibonacci-offsets N={N} (16 staggered calls, distinct buffers)",
@@ -323,11 +370,18 @@ def main():
                         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4)}})
             torch.cuda.empty_cache()
+        for N in wl.OFFSET_WORKLOAD["lengths"]:
+            r = offset_backward(N, reps=10)
+            sec.append({"workload": f"fibonacci-offsets backward N={N} (alpha = 1 + 7/15)", "value": round(r["gbs"], 2),
+                        "unit": "GB/s", "call_ms": round(r["ms"], 5), "alg_bytes_per_call": r["bytes"],
+                        "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4)}})
+            torch.cuda.empty_cache()
         for name in wl.OFFSET_VARIANTS:
             r = offset_variant_workload(name, reps=5, warmup=1)
             sec.append({"workload": f"offsets {name} N=2048 (16 calls, distinct buffers)",
                         "value": round(r["gbs"], 2), "unit": "GB/s", "call_ms": round(r["call_ms"], 5),
-                        "keys_per_query_max": r["keys"], "alg_bytes_per_call": r["bytes"],
+                        "keys_per_query_mean": r["keys"], "alg_bytes_per_call": r["bytes"],
                         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": PEAK_HBM_GBS,
                                      "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4)}})
             torch.cuda.empty_cache()

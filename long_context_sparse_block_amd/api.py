@@ -455,12 +455,66 @@ class BlockSparsePlan:
         return self.o, self.lse
 
 
+class BlockSparseBwdPlan:
+    """Pre-marshalled sparse_attn_bwd call on the buffers of a BlockSparsePlan
+    (its forward outputs o, lse) and an upstream gradient ``dout``; the mask
+    transpose is built once (``transpose()`` rebuilds it after a new mask)."""
+
+    def __init__(self, plan, dout):
+        B, H, Hkv, N, d = _check_qkv(plan.q, plan.k, plan.v)
+        self.device, self.plan, self.dout = plan.device, plan, dout
+        m = plan.mask
+        self.col_ptr = torch.empty(m.num_groups * m.num_blocks + 1, dtype=torch.int32, device=self.device)
+        self.row_idx = torch.empty(m.col_idx.numel(), dtype=torch.int32, device=self.device)
+        self.dq, self.dk, self.dv, self.delta = _grad_outputs(plan.q, plan.k)
+        self._lib = L.lib()
+        self._tr_args = (m.num_groups, m.num_blocks, _ptr(m.row_ptr), _ptr(m.col_idx), m.col_idx.numel(),
+                         _ptr(self.col_ptr), _ptr(self.row_idx), self.row_idx.numel())
+        q, k, v = plan.q, plan.k, plan.v
+        self._args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(plan.o), _ptr(plan.lse), _ptr(dout),
+                      _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.delta), B, H, Hkv, N, d,
+                      N // m.num_blocks, _strides(q, k, v, plan.o, dout, self.dq, self.dk, self.dv),
+                      _ptr(m.row_ptr), _ptr(m.col_idx), m.col_idx.numel(), _ptr(self.col_ptr), _ptr(self.row_idx),
+                      self.row_idx.numel(), m.num_groups, plan.mbs, plan.mhs, int(m.causal), plan.scale)
+        self.transpose()
+
+    def transpose(self):
+        _check(self._lib.sparse_attn_mask_transpose(*self._tr_args, _stream(self.device)),
+               "sparse_attn_mask_transpose")
+
+    def __call__(self):
+        _check(self._lib.sparse_attn_bwd(*self._args, _stream(self.device)), "sparse_attn_bwd")
+        return self.dq, self.dk, self.dv
+
+
+class OffsetBwdPlan:
+    """Pre-marshalled offset_attn_bwd call on the buffers of an OffsetPlan."""
+
+    def __init__(self, plan, offsets, dout, scale=None):
+        q, k, v = plan.q, plan.k, plan.v
+        B, H, Hkv, N, d = _check_qkv(q, k, v)
+        self.device = plan.device
+        offs = [int(x) for x in offsets]
+        self._arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
+        self.dq, self.dk, self.dv, self.delta = _grad_outputs(q, k)
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        self._args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(plan.o), _ptr(plan.lse), _ptr(dout),
+                      _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.delta), B, H, Hkv, N, d,
+                      _strides(q, k, v, plan.o, dout, self.dq, self.dk, self.dv), self._arr, len(offs), scale)
+        self._lib = L.lib()
+
+    def __call__(self):
+        _check(self._lib.offset_attn_bwd(*self._args, _stream(self.device)), "offset_attn_bwd")
+        return self.dq, self.dk, self.dv
+
+
 class OffsetPlan:
     """Pre-marshalled offset_attn_fwd call on fixed tensors (allocates nothing per call)."""
 
     def __init__(self, q, k, v, offsets, scale=None, rungs=None):
         B, H, Hkv, N, d = _check_qkv(q, k, v)
         self.device = q.device
+        self.q, self.k, self.v = q, k, v
         offs = [int(x) for x in offsets]
         self._arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
         self.o = torch.empty_like(q, memory_format=torch.contiguous_format)
