@@ -15,8 +15,10 @@
 //     products on v_mfma_f32_32x32x16_bf16, P and dS fed from the
 //     accumulators as B operands, the transposed A operands (K^T, Q^T, dO^T)
 //     by ds_read_b64_tr_b16 from LDS;
-//   * block-sparse fp32 and both offset kernels: one thread per row, plain
-//     fp32 arithmetic (exactness path; the offset kernels also take bf16).
+//   * offsets bf16: four adjacent lanes per row (coalesced 64-byte segments),
+//     16 rows per wave, distances four at a time;
+//   * block-sparse fp32 and offsets fp32: one thread per row, plain fp32
+//     arithmetic (exactness path).
 #include <math.h>
 
 #include <algorithm>
@@ -633,6 +635,162 @@ __global__ __launch_bounds__(256) void off_bwd_dkdv(BwdArgs a) {
   store_f<D, BF16>((T*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + s * a.st[TDV][2], dv);
 }
 
+// bf16 offset gradients: four lanes per row (lane 4 r + j holds 16-byte chunks
+// 4 c + j of its row), 16 rows per wave, so the 4 lanes reading one row are
+// adjacent (one 64-byte segment per group of 4 lanes); dot products are
+// reduced over the quad with DPP.  Distances are taken OB at a time (loads
+// first, then the arithmetic).
+constexpr int OB = 4;
+
+__device__ __forceinline__ void unpack8(const sa::u32x4& w, float* f) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[2 * j] = sa::bf16_lo(w[j]), f[2 * j + 1] = sa::bf16_hi(w[j]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void off_bwd_dq_bf16(BwdArgs a) {
+  constexpr int NC = D / 32;
+  const int tiles = (a.N + 63) / 64;
+  const int32_t bh = blockIdx.x / tiles;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, rq = lane >> 2, j = lane & 3;
+  const int64_t t = (int64_t)(blockIdx.x % tiles) * 64 + 16 * w + rq;
+  const bool live = t < a.N;
+  const int64_t tq = live ? t : a.N - 1;
+  const int32_t b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
+  const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+  const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+  const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1] + tq * a.st[TQ][2];
+  const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1] + tq * a.st[TDO][2];
+  sa::u32x4 qv[NC], gv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) qv[c] = *(const sa::u32x4*)(Q + 8 * (4 * c + j)), gv[c] = *(const sa::u32x4*)(G + 8 * (4 * c + j));
+  float acc[8 * NC];
+#pragma unroll
+  for (int x = 0; x < 8 * NC; ++x) acc[x] = 0.f;
+  const int64_t row = ((int64_t)b * a.H + h) * a.N + tq;
+  const float l2 = lse2_of(a.lse[row]), dd = a.delta[row];
+  for (int n0 = 0; n0 < a.noff; n0 += OB) {
+    sa::u32x4 kr[OB][NC], vr[OB][NC];
+    bool ok[OB];
+#pragma unroll
+    for (int u = 0; u < OB; ++u) {
+      const int n = min(n0 + u, a.noff - 1);
+      ok[u] = n0 + u < a.noff && tq >= a.offs[n];
+      const int64_t src = max(tq - a.offs[n], (int64_t)0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kr[u][c] = *(const sa::u32x4*)(K + src * a.st[TK][2] + 8 * (4 * c + j));
+        vr[u][c] = *(const sa::u32x4*)(V + src * a.st[TV][2] + 8 * (4 * c + j));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < OB; ++u) {
+      float dot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dot = sa::dot2_bf16(qv[c][x], kr[u][c][x], dot), dp = sa::dot2_bf16(gv[c][x], vr[u][c][x], dp);
+      dot = sa::quad_sum(dot);
+      dp = sa::quad_sum(dp);
+      const float ds = ok[u] ? exp2f(dot * a.c2 - l2) * (dp - dd) : 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float kf[8];
+        unpack8(kr[u][c], kf);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[8 * c + x] = fmaf(ds, kf[x], acc[8 * c + x]);
+      }
+    }
+  }
+  if (!live) return;
+  uint16_t* DQ = (uint16_t*)a.dq + b * a.st[TDQ][0] + h * a.st[TDQ][1] + t * a.st[TDQ][2];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    sa::u32x4 wv;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) wv[x] = sa::pack_bf16x2(acc[8 * c + 2 * x] * a.scale, acc[8 * c + 2 * x + 1] * a.scale);
+    *(sa::u32x4*)(DQ + 8 * (4 * c + j)) = wv;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void off_bwd_dkdv_bf16(BwdArgs a) {
+  constexpr int NC = D / 32;
+  const int tiles = (a.N + 63) / 64;
+  const int32_t bk = blockIdx.x / tiles;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, rk = lane >> 2, j = lane & 3;
+  const int64_t s = (int64_t)(blockIdx.x % tiles) * 64 + 16 * w + rk;
+  const bool live = s < a.N;
+  const int64_t sk = live ? s : a.N - 1;
+  const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv, rep = a.H / a.H_kv;
+  const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1] + sk * a.st[TK][2];
+  const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1] + sk * a.st[TV][2];
+  sa::u32x4 kv[NC], vv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kv[c] = *(const sa::u32x4*)(K + 8 * (4 * c + j)), vv[c] = *(const sa::u32x4*)(V + 8 * (4 * c + j));
+  float dk[8 * NC], dv[8 * NC];
+#pragma unroll
+  for (int x = 0; x < 8 * NC; ++x) dk[x] = dv[x] = 0.f;
+  for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+    const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+    const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+    const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
+    for (int n0 = 0; n0 < a.noff; n0 += OB) {
+      sa::u32x4 qr[OB][NC], gr[OB][NC];
+      float l2[OB], dd[OB];
+      bool ok[OB];
+#pragma unroll
+      for (int u = 0; u < OB; ++u) {
+        const int n = min(n0 + u, a.noff - 1);
+        const int64_t t = sk + a.offs[n];
+        ok[u] = n0 + u < a.noff && t < a.N;
+        const int64_t tt = min(t, (int64_t)a.N - 1);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          qr[u][c] = *(const sa::u32x4*)(Q + tt * a.st[TQ][2] + 8 * (4 * c + j));
+          gr[u][c] = *(const sa::u32x4*)(G + tt * a.st[TDO][2] + 8 * (4 * c + j));
+        }
+        l2[u] = lse2_of(a.lse[rowb + tt]);
+        dd[u] = a.delta[rowb + tt];
+      }
+#pragma unroll
+      for (int u = 0; u < OB; ++u) {
+        float dot = 0.f, dp = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) dot = sa::dot2_bf16(qr[u][c][x], kv[c][x], dot), dp = sa::dot2_bf16(gr[u][c][x], vv[c][x], dp);
+        dot = sa::quad_sum(dot);
+        dp = sa::quad_sum(dp);
+        const float p = ok[u] ? exp2f(dot * a.c2 - l2[u]) : 0.f;
+        const float ds = p * (dp - dd[u]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          float qf[8], gf[8];
+          unpack8(qr[u][c], qf);
+          unpack8(gr[u][c], gf);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) dk[8 * c + x] = fmaf(ds, qf[x], dk[8 * c + x]), dv[8 * c + x] = fmaf(p, gf[x], dv[8 * c + x]);
+        }
+      }
+    }
+  }
+  if (!live) return;
+  uint16_t* DK = (uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + s * a.st[TDK][2];
+  uint16_t* DV = (uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + s * a.st[TDV][2];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    sa::u32x4 w1, w2;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      w1[x] = sa::pack_bf16x2(dk[8 * c + 2 * x] * a.scale, dk[8 * c + 2 * x + 1] * a.scale);
+      w2[x] = sa::pack_bf16x2(dv[8 * c + 2 * x], dv[8 * c + 2 * x + 1]);
+    }
+    *(sa::u32x4*)(DK + 8 * (4 * c + j)) = w1;
+    *(sa::u32x4*)(DV + 8 * (4 * c + j)) = w2;
+  }
+}
+
 // ------------------------------------------------------------------ host ---
 template <typename F>
 sa_status launch(F kern, const BwdArgs& a, int64_t blocks, int threads, int lds, hipStream_t stream,
@@ -772,11 +930,13 @@ extern "C" sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k
   const int64_t tiles = ((int64_t)N + 255) / 256;
   const int64_t nq = (int64_t)B * H * tiles, nk = (int64_t)B * H_kv * tiles;
   if (dtype == SA_BF16) {
-    st = d == 64 ? launch(off_bwd_dq<64, true>, a, nq, 256, 0, stream, "off_bwd_dq")
-                 : launch(off_bwd_dq<128, true>, a, nq, 256, 0, stream, "off_bwd_dq");
+    const int64_t t64 = ((int64_t)N + 63) / 64;
+    const int64_t mq = (int64_t)B * H * t64, mk = (int64_t)B * H_kv * t64;
+    st = d == 64 ? launch(off_bwd_dq_bf16<64>, a, mq, 256, 0, stream, "off_bwd_dq_bf16")
+                 : launch(off_bwd_dq_bf16<128>, a, mq, 256, 0, stream, "off_bwd_dq_bf16");
     if (st != SA_OK) return st;
-    return d == 64 ? launch(off_bwd_dkdv<64, true>, a, nk, 256, 0, stream, "off_bwd_dkdv")
-                   : launch(off_bwd_dkdv<128, true>, a, nk, 256, 0, stream, "off_bwd_dkdv");
+    return d == 64 ? launch(off_bwd_dkdv_bf16<64>, a, mk, 256, 0, stream, "off_bwd_dkdv_bf16")
+                   : launch(off_bwd_dkdv_bf16<128>, a, mk, 256, 0, stream, "off_bwd_dkdv_bf16");
   }
   st = d == 64 ? launch(off_bwd_dq<64, false>, a, nq, 256, 0, stream, "off_bwd_dq")
                : launch(off_bwd_dq<128, false>, a, nq, 256, 0, stream, "off_bwd_dq");
