@@ -332,14 +332,23 @@ sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, con
  * sparse_attn_mask_transpose).
  *   q, k, v, o, lse  the forward's inputs and outputs; dout = dO [B, H, N, d]
  *   dq [B, H, N, d], dk, dv [B, H_kv, N, d]  DEVICE, written (input dtype)
- *   delta            DEVICE fp32 [B, H, N] workspace, written with D
+ *   workspace        DEVICE, 16-byte aligned, workspace_bytes >=
+ *                    sparse_attn_bwd_workspace_bytes(B, H, H_kv, N, d, block)
+ *                    (else SA_ERR_CAPACITY): D, the dK/dV work list, and fp32
+ *                    partial dK/dV of key blocks listed by more than 32 query
+ *                    blocks (those are split over several workgroups and their
+ *                    partial sums added with fp32 atomics, so their low-order
+ *                    bits may differ from run to run)
  *   strides          HOST int64 [8][3] for q, k, v, o, dout, dq, dk, dv
  *                    (batch, head, sequence strides in elements) or NULL
  * Other arguments, layouts, supported sizes and errors as for sparse_attn_fwd.
  */
+int64_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                        int32_t block);
 sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
-                          const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
-                          int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d, int32_t block,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                          int64_t workspace_bytes, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                          int32_t block,
                           const int64_t* strides, const int32_t* row_ptr, const int32_t* col_idx,
                           int64_t col_capacity, const int32_t* col_ptr, const int32_t* row_idx,
                           int64_t row_capacity, int32_t num_groups, int64_t mask_batch_stride,
@@ -347,8 +356,8 @@ sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k, const voi
 
 /*
  * Offset attention backward over the table used by offset_attn_fwd.
- * Tensors, delta and strides as for sparse_attn_bwd; offsets as for
- * offset_attn_fwd.
+ * Tensors and strides as for sparse_attn_bwd; delta is a DEVICE fp32
+ * [B, H, N] workspace (written with D); offsets as for offset_attn_fwd.
  */
 sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
                           const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,

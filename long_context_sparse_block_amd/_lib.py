@@ -85,7 +85,8 @@ SIGNATURES = {
                                       ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32),
                                       ctypes.POINTER(_f32), _i32, _f32, _p]),
     "sparse_attn_mask_transpose": (_i32, [_i32, _i32, _p, _p, _i64, _p, _p, _i64, _p]),
-    "sparse_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+    "sparse_attn_bwd_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "sparse_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(_i64), _p, _p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i32, _f32,
                                _p]),
     "offset_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,

@@ -247,6 +247,13 @@ def _grad_outputs(q, k):
             torch.empty(q.shape[:3], dtype=torch.float32, device=q.device))
 
 
+def _bwd_workspace(B, H, Hkv, N, d, block, device):
+    n = L.lib().sparse_attn_bwd_workspace_bytes(B, H, Hkv, N, d, block)
+    if n < 0:
+        raise SparseAttnError(int(n), "sparse_attn_bwd_workspace_bytes")
+    return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
 def sparse_attn_bwd(q, k, v, o, lse, dout, mask, transpose=None, scale=None, mask_batch_stride=0,
                     mask_head_stride=0):
     """Gradients (dq, dk, dv) of block-sparse attention; ``transpose`` is the
@@ -255,10 +262,11 @@ def sparse_attn_bwd(q, k, v, o, lse, dout, mask, transpose=None, scale=None, mas
     block = N // mask.num_blocks
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     col_ptr, row_idx = transpose if transpose is not None else sparse_attn_mask_transpose(mask)
-    dq, dk, dv, delta = _grad_outputs(q, k)
+    dq, dk, dv, _ = _grad_outputs(q, k)
+    ws = _bwd_workspace(B, H, Hkv, N, d, block, q.device)
     st = L.lib().sparse_attn_bwd(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(delta), B, H, Hkv, N, d, block, _strides(q, k, v, o, dout, dq, dk, dv), _ptr(mask.row_ptr),
+        _ptr(ws), ws.numel(), B, H, Hkv, N, d, block, _strides(q, k, v, o, dout, dq, dk, dv), _ptr(mask.row_ptr),
         _ptr(mask.col_idx), mask.col_idx.numel(), _ptr(col_ptr), _ptr(row_idx), row_idx.numel(),
         mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal), scale, _stream(q.device))
     _check(st, "sparse_attn_bwd")
@@ -466,13 +474,14 @@ class BlockSparseBwdPlan:
         m = plan.mask
         self.col_ptr = torch.empty(m.num_groups * m.num_blocks + 1, dtype=torch.int32, device=self.device)
         self.row_idx = torch.empty(m.col_idx.numel(), dtype=torch.int32, device=self.device)
-        self.dq, self.dk, self.dv, self.delta = _grad_outputs(plan.q, plan.k)
+        self.dq, self.dk, self.dv, _ = _grad_outputs(plan.q, plan.k)
+        self.ws = _bwd_workspace(B, H, Hkv, N, d, N // m.num_blocks, self.device)
         self._lib = L.lib()
         self._tr_args = (m.num_groups, m.num_blocks, _ptr(m.row_ptr), _ptr(m.col_idx), m.col_idx.numel(),
                          _ptr(self.col_ptr), _ptr(self.row_idx), self.row_idx.numel())
         q, k, v = plan.q, plan.k, plan.v
         self._args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(plan.o), _ptr(plan.lse), _ptr(dout),
-                      _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.delta), B, H, Hkv, N, d,
+                      _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.ws), self.ws.numel(), B, H, Hkv, N, d,
                       N // m.num_blocks, _strides(q, k, v, plan.o, dout, self.dq, self.dk, self.dv),
                       _ptr(m.row_ptr), _ptr(m.col_idx), m.col_idx.numel(), _ptr(self.col_ptr), _ptr(self.row_idx),
                       self.row_idx.numel(), m.num_groups, plan.mbs, plan.mhs, int(m.causal), plan.scale)

@@ -51,6 +51,11 @@ struct BwdArgs {
   float scale, c2;  // c2 = scale * log2(e)
   int32_t noff;
   int32_t offs[SA_MAX_OFFSETS];
+  // block-sparse dK/dV work list: columns (b, kvh, j) split into chunks of
+  // `chunk` entries; pre[c] = first work item of column c (exclusive scan)
+  int32_t* pre;
+  float* acc;  // fp32 [2][B][H_kv][N][d]: partial dK, dV of split columns
+  int32_t chunk;
 };
 
 enum { TQ = 0, TK = 1, TV = 2, TO = 3, TDO = 4, TDQ = 5, TDK = 6, TDV = 7 };
@@ -464,8 +469,75 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
     }
 }
 
-// dk, dv: one workgroup (BLK/32 waves) per key block, a wave per 32 keys,
-// over the q heads of the K/V head and the query blocks that list the block.
+// Column c = (b * H_kv + kvh) * nb + j of the dK/dV work: its entries are the
+// transposed-mask lists of key block j for the q heads h of K/V head kvh, in
+// head order.  Number of entries (before skipping unusable ones).
+__device__ __forceinline__ int32_t column_len(const BwdArgs& a, int32_t b, int32_t kvh, int32_t j) {
+  const int32_t rep = a.H / a.H_kv;
+  int32_t n = 0;
+  for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+    int32_t e0, e1;
+    col_range(a, (int64_t)b * a.mbs + (int64_t)h * a.mhs, j, e0, e1);
+    n += e1 - e0;
+  }
+  return n;
+}
+
+// One wave per column: pre[c + 1] = number of work items (chunks) of column c;
+// a column split in several chunks gets its fp32 partial rows zeroed.
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void dkdv_plan_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
+  if (c >= cols) return;
+  const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
+  const int32_t len = column_len(a, bk / a.H_kv, bk % a.H_kv, j);
+  const int32_t chunks = max(1, (len + a.chunk - 1) / a.chunk);
+  if (lane == 0) a.pre[c + 1] = chunks;
+  if (chunks > 1) {
+    const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
+    float* r0 = a.acc + ((int64_t)bk * a.N + (int64_t)j * BLK) * D;
+    for (int x = lane; x < BLK * D / 4; x += 64) {
+      *(sa::f32x4*)(r0 + 4 * x) = sa::f32x4{0.f, 0.f, 0.f, 0.f};
+      *(sa::f32x4*)(r0 + plane + 4 * x) = sa::f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// One wave per split column: fp32 partial sums -> bf16 dk (scaled), dv.
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
+  if (c >= cols || a.pre[c + 1] - a.pre[c] <= 1) return;
+  const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
+  const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
+  const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
+  const float* r0 = a.acc + ((int64_t)bk * a.N + (int64_t)j * BLK) * D;
+  for (int x = lane; x < BLK * D / 8; x += 64) {
+    const int r = x / (D / 8), c8 = x % (D / 8);
+    const int64_t key = (int64_t)j * BLK + r;
+    const float* pk = r0 + r * D + 8 * c8;
+    const float* pv = pk + plane;
+    sa::u32x4 wk, wv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wk[e] = sa::pack_bf16x2(pk[2 * e] * a.scale, pk[2 * e + 1] * a.scale);
+      wv[e] = sa::pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+    }
+    *(sa::u32x4*)((uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + key * a.st[TDK][2] + 8 * c8) = wk;
+    *(sa::u32x4*)((uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + key * a.st[TDV][2] + 8 * c8) = wv;
+  }
+}
+
+// dk, dv: persistent workgroups (BLK/32 waves, a wave per 32 keys of the key
+// block) take work items w = chunk of column c: entries [chunk * C, chunk * C
+// + C) of the column's list, so that a key block listed by many query blocks
+// (a global block) is shared by several workgroups.  A column with one chunk
+// writes its bf16 rows directly; the chunks of a split column add their fp32
+// partials into `acc` (converted afterwards).
 template <int D, int BLK>
 __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
   using L = TileLds<D>;
@@ -476,88 +548,123 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
   float* ls = (float*)(smem + 2 * BLK * 2 * D);
   float* dls = ls + BLK;
   const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
-  const int32_t bk = blockIdx.x / a.nb, j = blockIdx.x % a.nb;
-  const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv, rep = a.H / a.H_kv;
-  const int64_t sk = (int64_t)j * BLK + 32 * w + (lane & 31);  // this lane's key (C column)
-  const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
-  const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
-  sa::u32x4 kb_[NU], vb_[NU];  // B operands: column = key, k = d
+  const int32_t rep = a.H / a.H_kv;
+  const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
+  const int32_t items = a.pre[cols];
+  for (int32_t item = blockIdx.x; item < items; item += gridDim.x) {
+    // column of the item: the last c with pre[c] <= item
+    int64_t lo = 0, hi = cols;
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (a.pre[mid] <= item)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int64_t c = sa::uniform((int32_t)lo);
+    const int32_t chunk = sa::uniform(item - a.pre[c]);
+    const bool split = a.pre[c + 1] - a.pre[c] > 1;
+    const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
+    const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
+    const int32_t f0 = chunk * a.chunk, f1 = f0 + a.chunk;  // flat entry range of this item
+    const int64_t sk = (int64_t)j * BLK + 32 * w + (lane & 31);  // this lane's key (C column)
+    const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
+    const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
+    sa::u32x4 kb_[NU], vb_[NU];  // B operands: column = key, k = d
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    kb_[u] = *(const sa::u32x4*)(K + sk * a.st[TK][2] + 16 * u + 8 * hl);
-    vb_[u] = *(const sa::u32x4*)(V + sk * a.st[TV][2] + 16 * u + 8 * hl);
-  }
-  sa::f32x16 dk[NT], dv[NT];
+    for (int u = 0; u < NU; ++u) {
+      kb_[u] = *(const sa::u32x4*)(K + sk * a.st[TK][2] + 16 * u + 8 * hl);
+      vb_[u] = *(const sa::u32x4*)(V + sk * a.st[TV][2] + 16 * u + 8 * hl);
+    }
+    sa::f32x16 dk[NT], dv[NT];
 #pragma unroll
-  for (int dt = 0; dt < NT; ++dt) dk[dt] = sa::f32x16{}, dv[dt] = sa::f32x16{};
-  for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
-    const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
-    const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
-    const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
-    const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
-    int32_t e0, e1;
-    col_range(a, g, j, e0, e1);
-    for (int32_t e = e0; e < e1; ++e) {
-      const int32_t qb = sa::uniform(a.row_idx[e]);
-      if (qb < 0 || qb >= a.nb || (a.causal && qb < j)) continue;
-      __syncthreads();
-      stage_rows<D>(qs, Q, (int64_t)qb * BLK, a.st[TQ][2], BLK, tid, NTH);
-      stage_rows<D>(gs, G, (int64_t)qb * BLK, a.st[TDO][2], BLK, tid, NTH);
-      for (int r = tid; r < BLK; r += NTH) {
-        ls[r] = lse2_of(a.lse[rowb + (int64_t)qb * BLK + r]);
-        dls[r] = a.delta[rowb + (int64_t)qb * BLK + r];
-      }
-      __syncthreads();
-#pragma unroll 1
-      for (int qt = 0; qt < BLK / 32; ++qt) {
-        // S and dP [32 queries x 32 keys]
-        sa::f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
-          dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vb_[u], dp);
+    for (int dt = 0; dt < NT; ++dt) dk[dt] = sa::f32x16{}, dv[dt] = sa::f32x16{};
+    int32_t fbase = 0;  // flat index of the current head's first entry
+    for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+      const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+      const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
+      const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+      const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
+      int32_t e0, e1;
+      col_range(a, g, j, e0, e1);
+      const int32_t lo_e = max(e0, e0 + f0 - fbase), hi_e = min(e1, e0 + f1 - fbase);
+      fbase += e1 - e0;
+      for (int32_t e = lo_e; e < hi_e; ++e) {
+        const int32_t qb = sa::uniform(a.row_idx[e]);
+        if (qb < 0 || qb >= a.nb || (a.causal && qb < j)) continue;
+        __syncthreads();
+        stage_rows<D>(qs, Q, (int64_t)qb * BLK, a.st[TQ][2], BLK, tid, NTH);
+        stage_rows<D>(gs, G, (int64_t)qb * BLK, a.st[TDO][2], BLK, tid, NTH);
+        for (int r = tid; r < BLK; r += NTH) {
+          ls[r] = lse2_of(a.lse[rowb + (int64_t)qb * BLK + r]);
+          dls[r] = a.delta[rowb + (int64_t)qb * BLK + r];
         }
-        float p[16], ds[16];
+        __syncthreads();
+#pragma unroll 1
+        for (int qt = 0; qt < BLK / 32; ++qt) {
+          // S and dP [32 queries x 32 keys]
+          sa::f32x16 s = {}, dp = {};
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
+            dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vb_[u], dp);
+          }
+          float p[16], ds[16];
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
+            const sa::f32x4 l4 = *(const sa::f32x4*)(ls + q4);
+            const sa::f32x4 d4 = *(const sa::f32x4*)(dls + q4);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+              const int r = 4 * r4 + cc;
+              const int64_t tq = (int64_t)qb * BLK + q4 + cc;
+              p[r] = (a.causal && sk > tq) ? 0.f : exp2f(s[r] * a.c2 - l4[cc]);
+              ds[r] = p[r] * (dp[r] - d4[cc]);
+            }
+          }
+          // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) {
+              dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
+              dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
+            }
+          }
+        }
+      }
+    }
+    // C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's key
+    if (!split) {
+      uint16_t* DK = (uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + sk * a.st[TDK][2];
+      uint16_t* DV = (uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + sk * a.st[TDV][2];
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
-          const sa::f32x4 l4 = *(const sa::f32x4*)(ls + q4);
-          const sa::f32x4 d4 = *(const sa::f32x4*)(dls + q4);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * r4 + c;
-            const int64_t tq = (int64_t)qb * BLK + q4 + c;
-            p[r] = (a.causal && sk > tq) ? 0.f : exp2f(s[r] * a.c2 - l4[c]);
-            ds[r] = p[r] * (dp[r] - d4[c]);
-          }
+          const sa::f32x16& x = dk[dt];
+          const sa::f32x16& y = dv[dt];
+          const int r = 4 * r4;
+          *(sa::u32x2*)(DK + 32 * dt + 8 * r4 + 4 * hl) = sa::u32x2{
+              sa::pack_bf16x2(x[r] * a.scale, x[r + 1] * a.scale), sa::pack_bf16x2(x[r + 2] * a.scale, x[r + 3] * a.scale)};
+          *(sa::u32x2*)(DV + 32 * dt + 8 * r4 + 4 * hl) =
+              sa::u32x2{sa::pack_bf16x2(y[r], y[r + 1]), sa::pack_bf16x2(y[r + 2], y[r + 3])};
         }
-        // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
+    } else {
+      const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
+      float* pk = a.acc + ((int64_t)bk * a.N + sk) * D;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
+      for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
-          for (int dt = 0; dt < NT; ++dt) {
-            dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
-            dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int x = 32 * dt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          atomicAdd(pk + x, dk[dt][r]);
+          atomicAdd(pk + plane + x, dv[dt][r]);
         }
-      }
     }
   }
-  uint16_t* DK = (uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + sk * a.st[TDK][2];
-  uint16_t* DV = (uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + sk * a.st[TDV][2];
-#pragma unroll
-  for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const sa::f32x16& x = dk[dt];
-      const sa::f32x16& y = dv[dt];
-      const int r = 4 * r4;
-      *(sa::u32x2*)(DK + 32 * dt + 8 * r4 + 4 * hl) = sa::u32x2{
-          sa::pack_bf16x2(x[r] * a.scale, x[r + 1] * a.scale), sa::pack_bf16x2(x[r + 2] * a.scale, x[r + 3] * a.scale)};
-      *(sa::u32x2*)(DV + 32 * dt + 8 * r4 + 4 * hl) =
-          sa::u32x2{sa::pack_bf16x2(y[r], y[r + 1]), sa::pack_bf16x2(y[r + 2], y[r + 3])};
-    }
 }
 
 // --------------------------------------------------------------- offsets ---
@@ -851,15 +958,45 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
   if (bf16) {
     st = launch(bsa_bwd_dq_bf16<D, BLK>, a, nq, 2 * BLK, 2 * BLK * 2 * D, stream, "bsa_bwd_dq_bf16");
     if (st != SA_OK) return st;
-    return launch(bsa_bwd_dkdv_bf16<D, BLK>, a, nk, 2 * BLK, 2 * BLK * 2 * D + 2 * BLK * 4, stream,
-                  "bsa_bwd_dkdv_bf16");
+    const int64_t wblocks = (nk + 3) / 4;
+    st = launch(dkdv_plan_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_plan_kernel");
+    if (st != SA_OK) return st;
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.pre, nk);
+    st = sa_host::check_launch("scan_kernel");
+    if (st != SA_OK) return st;
+    // persistent workgroups; the item count lives on the device
+    st = launch(bsa_bwd_dkdv_bf16<D, BLK>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK,
+                2 * BLK * 2 * D + 2 * BLK * 4, stream, "bsa_bwd_dkdv_bf16");
+    if (st != SA_OK) return st;
+    return launch(dkdv_convert_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_convert_kernel");
   }
   st = launch(bsa_bwd_dq_f32<D, BLK>, a, nq, BLK, 0, stream, "bsa_bwd_dq_f32");
   if (st != SA_OK) return st;
   return launch(bsa_bwd_dkdv_f32<D, BLK>, a, nk, BLK, 0, stream, "bsa_bwd_dkdv_f32");
 }
 
+// Workspace of sparse_attn_bwd: delta fp32 [B*H*N] | pre int32 [B*H_kv*nb + 1]
+// | acc fp32 [2][B*H_kv*N*d], each part 256-byte aligned.
+struct WsLayout {
+  int64_t delta, pre, acc, total;
+};
+WsLayout ws_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int64_t block) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  WsLayout l;
+  l.delta = 0;
+  l.pre = up(B * H * N * 4);
+  l.acc = l.pre + up((B * H_kv * (N / block) + 1) * 4);
+  l.total = l.acc + up(2 * B * H_kv * N * d * 4);
+  return l;
+}
+
 }  // namespace
+
+extern "C" int64_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                                   int32_t block) {
+  if (B < 1 || H < 1 || H_kv < 1 || N < 1 || d < 1 || block < 1) return SA_ERR_INVALID;
+  return ws_layout(B, H, H_kv, N, d, block).total;
+}
 
 extern "C" sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, const int32_t* row_ptr,
                                                 const int32_t* col_idx, int64_t col_capacity, int32_t* col_ptr,
@@ -883,16 +1020,26 @@ extern "C" sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_
 
 extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k, const void* v, const void* o,
                                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                     float* delta, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                     void* workspace, int64_t workspace_bytes, int32_t B, int32_t H,
+                                     int32_t H_kv, int32_t N, int32_t d,
                                      int32_t block, const int64_t* strides, const int32_t* row_ptr,
                                      const int32_t* col_idx, int64_t col_capacity, const int32_t* col_ptr,
                                      const int32_t* row_idx, int64_t row_capacity, int32_t num_groups,
                                      int64_t mask_batch_stride, int64_t mask_head_stride, int32_t causal,
                                      float scale, hipStream_t stream) {
   BwdArgs a = {};
-  if (!row_ptr || !col_idx || !col_ptr || !row_idx) return SA_ERR_NULL;
-  sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, strides, scale);
+  if (!row_ptr || !col_idx || !col_ptr || !row_idx || !workspace) return SA_ERR_NULL;
+  if (!sa_host::aligned16(workspace) || block < 1) return SA_ERR_INVALID;
+  const WsLayout wsl = ws_layout(B > 0 ? B : 1, H > 0 ? H : 1, H_kv > 0 ? H_kv : 1, N > 0 ? N : 1,
+                                 d > 0 ? d : 1, block);
+  if (workspace_bytes < wsl.total) return SA_ERR_CAPACITY;
+  uint8_t* ws = (uint8_t*)workspace;
+  sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, (float*)(ws + wsl.delta), B, H, H_kv,
+                             N, d, strides, scale);
   if (st != SA_OK) return st;
+  a.pre = (int32_t*)(ws + wsl.pre);
+  a.acc = (float*)(ws + wsl.acc);
+  a.chunk = 32;
   if (block < 1 || causal < 0 || causal > 1 || col_capacity < 0 || row_capacity < 0) return SA_ERR_INVALID;
   if (num_groups < 1 || mask_batch_stride < 0 || mask_head_stride < 0) return SA_ERR_INVALID;
   if ((int64_t)(B - 1) * mask_batch_stride + (int64_t)(H - 1) * mask_head_stride >= num_groups)
