@@ -22,9 +22,11 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_host.h"
+
 
 namespace {
 
@@ -39,6 +41,7 @@ struct BwdArgs {
   void* dv;
   const float* lse;
   float* delta;
+  sa::f32x2* stat;  // block-sparse bf16: per row {lse log2(e) (+inf if empty), D}
   int64_t st[8][3];  // q k v o dout dq dk dv: batch, head, sequence strides (elements)
   const int32_t* row_ptr;
   const int32_t* col_idx;
@@ -116,8 +119,9 @@ __device__ __forceinline__ void store_f(typename Elem<BF16>::T* p, const float* 
 __device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * sa::kLog2e; }
 
 // ---------------------------------------------------------------- delta ----
-// D[b, h, t] = <dO_t, o_t>; D/8 lanes per row, 8 elements each.
-template <int D, bool BF16>
+// D[b, h, t] = <dO_t, o_t>; D/8 lanes per row, 8 elements each.  STAT: store
+// the pair {lse log2(e), D} of the row instead of D alone.
+template <int D, bool BF16, bool STAT>
 __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   typedef typename Elem<BF16>::T T;
   constexpr int LPR = D / 8;
@@ -137,7 +141,12 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   for (int j = 0; j < 8; ++j) s = fmaf(x[j], y[j], s);
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
-  if (live && part == 0) a.delta[rr] = s;
+  if (live && part == 0) {
+    if constexpr (STAT)
+      a.stat[rr] = sa::f32x2{lse2_of(a.lse[rr]), s};
+    else
+      a.delta[rr] = s;
+  }
 }
 
 // ------------------------------------------------------- mask transpose ----
@@ -375,16 +384,40 @@ struct TileLds {
   }
 };
 
-// Copy rows [r0, r0 + R) of a bf16 tensor (row stride rs elements) into a
-// swizzled LDS tile; nthr threads cooperate.
-template <int D>
-__device__ __forceinline__ void stage_rows(uint8_t* t, const uint16_t* src, int64_t r0, int64_t rs, int R,
-                                           int tid, int nthr) {
-  constexpr int CPR = D / 8;
-  for (int u = tid; u < R * CPR; u += nthr) {
-    const int r = u / CPR, c = u % CPR;
-    *(sa::u32x4*)(t + r * (2 * D) + bswz(c, r) * 16) = *(const sa::u32x4*)(src + (r0 + r) * rs + 8 * c);
+// Direct (DMA) copies of one 64-row bf16 tile into a swizzled LDS tile.  Wave
+// w of NW issues JN copies of 64 16-byte chunks; chunk u = 64 (j NW + w) + lane
+// of copy j is row u / CPR, slot u % CPR, so one per-lane source offset (row
+// r0 = (64 w + lane) / CPR, logical chunk slot ^ (r0 & 7)) serves every copy:
+// copy j reads RPC j rows further down (RPC a multiple of 8 keeps the swizzle)
+// and lands j NW KiB further into the tile.
+template <int D, int NW>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int JN = CPR / NW;         // copies per wave per tile
+  static constexpr int RPC = NW * 64 / CPR;   // rows between a wave's copies
+  static constexpr int TB = 64 * 2 * D;       // bytes of one tile
+  static_assert(JN >= 1 && RPC % 8 == 0, "tile split");
+  static __device__ __forceinline__ uint32_t lane_off(int w, int lane, int64_t rs) {
+    const int r0 = (64 * w + lane) / CPR, p = lane % CPR;
+    return (uint32_t)(r0 * rs * 2) + 16u * (uint32_t)(p ^ (r0 & 7));
   }
+  static __device__ __forceinline__ void copy(const uint16_t* src, int64_t rs, uint32_t off, uint32_t lds, int w) {
+#pragma unroll
+    for (int j = 0; j < JN; ++j) sa::dma16((const char*)src + (int64_t)j * RPC * rs * 2, off, lds + (j * NW + w) * 1024);
+  }
+};
+
+// Barrier that leaves outstanding direct copies in flight; ordering is by
+// explicit "s_waitcnt vmcnt".
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Wait until at most c * J vector memory operations of this wave are
+// outstanding (c in {0, 1}).
+template <int J>
+__device__ __forceinline__ void wait_units(int c) {
+  if (c > 0)
+    sa::vm_wait<J>();
+  else
+    sa::vm_wait<0>();
 }
 
 // pack C entries 8s .. 8s+7 into a bf16 B operand
@@ -393,66 +426,147 @@ __device__ __forceinline__ sa::u32x4 pack8(const float* x) {
                    sa::pack_bf16x2(x[6], x[7])};
 }
 
-// dq: one workgroup (BLK/32 waves) per query block, a wave per 32 queries.
-template <int D, int BLK>
+// The two 32-row halves of a 64-row tile.  With SPLIT the diagonal (causal)
+// tile runs a variant of its own and the others skip the mask; with ILV both
+// halves sit in one basic block so that their MFMAs and VALU work interleave
+// (more registers).
+#ifndef SA_BWD_SPLIT64
+#define SA_BWD_SPLIT64 1
+#endif
+#ifndef SA_BWD_SPLIT128
+#define SA_BWD_SPLIT128 0
+#endif
+#ifndef SA_BWD_ILV64
+#define SA_BWD_ILV64 0
+#endif
+#ifndef SA_BWD_ILV128
+#define SA_BWD_ILV128 0
+#endif
+template <int D, typename F>
+__device__ __forceinline__ void bwd_tile(bool diag, F& half) {
+  constexpr bool SPLIT = D == 64 ? SA_BWD_SPLIT64 : SA_BWD_SPLIT128;
+  constexpr bool ILV = D == 64 ? SA_BWD_ILV64 : SA_BWD_ILV128;
+  auto run = [&](auto mask_tag) {
+    if constexpr (ILV) {
+      half(0, mask_tag);
+      half(1, mask_tag);
+    } else {
+#pragma unroll 1
+      for (int x = 0; x < 2; ++x) half(x, mask_tag);
+    }
+  };
+  if constexpr (SPLIT) {
+    if (diag)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  } else {
+    run(std::true_type{});
+  }
+}
+
+// dq: one workgroup (BLK/32 waves) per query block, a wave per 32 queries.  The
+// row's key blocks are walked in 64-row tiles of K and V, copied global -> LDS
+// by direct loads into a ring of S slots: tile n + S - 1 is in flight while
+// tile n is used.  Entries whose block is unusable (out of range, or after the
+// query block when causal) load a safe tile and skip the arithmetic.
+template <int D, int BLK, int S>
 __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
   using L = TileLds<D>;
-  constexpr int NU = D / 16, NT = D / 32, NTH = 2 * BLK;
+  constexpr int NW = BLK / 32, NU = D / 16, NT = D / 32, SUBS = BLK / 64;
+  using M = TileDma<D, NW>;
+  constexpr int SLOT = 2 * M::TB;  // K tile, V tile
+  constexpr int CP = 2 * M::JN;    // copies per wave per tile
+  static_assert(S == 2 || S == 3, "ring slots");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* ks = smem;
-  uint8_t* vs = smem + BLK * 2 * D;
   const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
   const int32_t bh = blockIdx.x / a.nb, i = blockIdx.x % a.nb;
   const int32_t b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
   const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
-  const int64_t tq = (int64_t)i * BLK + 32 * w + (lane & 31);  // this lane's query (C column)
+  const int qoff = 32 * w + (lane & 31);           // this lane's query inside the block
+  const int64_t tq = (int64_t)i * BLK + qoff;      // ... and in the sequence (C column)
   const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
   const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
   const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
   const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
+  const int64_t ks2 = a.st[TK][2], vs2 = a.st[TV][2];
   sa::u32x4 qb[NU], gb[NU];  // B operands: column = query, k = d 16u + 8(l/32) ..
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     qb[u] = *(const sa::u32x4*)(Q + tq * a.st[TQ][2] + 16 * u + 8 * hl);
     gb[u] = *(const sa::u32x4*)(G + tq * a.st[TDO][2] + 16 * u + 8 * hl);
   }
-  const int64_t row = ((int64_t)b * a.H + h) * a.N + tq;
-  const float l2 = lse2_of(a.lse[row]), dd = a.delta[row];
+  const sa::f32x2 st2 = *(const sa::f32x2*)(a.stat + ((int64_t)b * a.H + h) * a.N + tq);
+  const float l2 = st2[0], dd = st2[1];
   sa::f32x16 acc[NT];
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::f32x16{};
+  const uint32_t offK = M::lane_off(w, lane, ks2), offV = M::lane_off(w, lane, vs2);
+  const uint32_t ring = sa::lds_addr(smem);
   int32_t e0, e1;
   row_range(a, g, i, e0, e1);
-  for (int32_t e = e0; e < e1; ++e) {
-    const int32_t kb = sa::uniform(a.col_idx[e]);
-    if (kb < 0 || kb >= a.nb || (a.causal && kb > i)) continue;
-    __syncthreads();
-    stage_rows<D>(ks, K, (int64_t)kb * BLK, a.st[TK][2], BLK, tid, NTH);
-    stage_rows<D>(vs, V, (int64_t)kb * BLK, a.st[TV][2], BLK, tid, NTH);
-    __syncthreads();
-#pragma unroll 1
-    for (int kt = 0; kt < BLK / 32; ++kt) {
-      // S^T and dP^T [32 keys x 32 queries]
-      sa::f32x16 s = {}, dp = {};
+  const int32_t limit = a.causal ? i + 1 : a.nb;  // usable key blocks are < limit
+  bool first = true;
+  for (int32_t base = e0; base < e1; base += 64) {
+    const int cnt = min(64, e1 - base);
+    const int32_t lst = lane < cnt ? a.col_idx[base + lane] : -1;  // entry base + x in lane x
+    // the loads above complete here, before any copy is in flight
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        s = sa::mfma32(L::rows_a(ks, 32 * kt, u, lane), qb[u], s);
-        dp = sa::mfma32(L::rows_a(vs, 32 * kt, u, lane), gb[u], dp);
-      }
-      float ds[16];
+    for (int u = 0; u < NU; ++u) sa::keep(qb[u]), sa::keep(gb[u]);
+    sa::keep(lst), sa::keep(l2), sa::keep(dd);
+    if (!first) ring_barrier();  // every wave is done with the ring
+    first = false;
+    const int T = cnt * SUBS;
+    auto tile_kb = [&](int m) -> int32_t {
+      const int32_t kb = sa::readlane(lst, m / SUBS);
+      return (uint32_t)kb < (uint32_t)limit ? kb : -1;
+    };
+    auto issue = [&](int m) {
+      const int32_t kb = tile_kb(m);
+      const int64_t r0 = (int64_t)(kb < 0 ? i : kb) * BLK + 64 * (m % SUBS);
+      const uint32_t dst = ring + (m % S) * SLOT;
+      M::copy(K + r0 * ks2, ks2, offK, dst, w);
+      M::copy(V + r0 * vs2, vs2, offV, dst + M::TB, w);
+    };
+    issue(0);
+    if (S > 2 && T > 1) issue(1);
+    for (int n = 0; n < T; ++n) {
+      wait_units<CP>(S > 2 && n + 1 < T);
+      ring_barrier();
+      if (n + S - 1 < T) issue(n + S - 1);
+      const int32_t kb = tile_kb(n);
+      if (kb < 0) continue;
+      const uint8_t* ks = smem + (n % S) * SLOT;
+      const uint8_t* vs = ks + M::TB;
+      const int ksub = 64 * (n % SUBS);
+      const bool diag = a.causal && kb == i;
+      // one 32-key half; MASK: apply the causal triangle when diag
+      auto half = [&](int kt, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        // S^T and dP^T [32 keys x 32 queries]
+        sa::f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = (int64_t)kb * BLK + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float p = (a.causal && key > tq) ? 0.f : exp2f(s[r] * a.c2 - l2);
-        ds[r] = p * (dp[r] - dd);
-      }
-      // dQ^T [d x queries] += K^T [d x keys] dS^T [keys x queries]
+        for (int u = 0; u < NU; ++u) {
+          s = sa::mfma32(L::rows_a(ks, 32 * kt, u, lane), qb[u], s);
+          dp = sa::mfma32(L::rows_a(vs, 32 * kt, u, lane), gb[u], dp);
+        }
+        float ds[16];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const sa::u32x4 bo = pack8(ds + 8 * st);
+        for (int r = 0; r < 16; ++r) {
+          const float p = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -l2));
+          ds[r] = p * (dp[r] - dd);
+          // keys after the query
+          if (MASK && diag && ksub + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3) > qoff) ds[r] = 0.f;
+        }
+        // dQ^T [d x queries] += K^T [d x keys] dS^T [keys x queries]
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::mfma32(L::rows_tr(ks, 32 * kt, st, dt, lane), bo, acc[dt]);
-      }
+        for (int st = 0; st < 2; ++st) {
+          const sa::u32x4 bo = pack8(ds + 8 * st);
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::mfma32(L::rows_tr(ks, 32 * kt, st, dt, lane), bo, acc[dt]);
+        }
+      };
+      bwd_tile<D>(diag, half);
     }
   }
   // C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's query
@@ -534,23 +648,32 @@ __global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
 
 // dk, dv: persistent workgroups (BLK/32 waves, a wave per 32 keys of the key
 // block) take work items w = chunk of column c: entries [chunk * C, chunk * C
-// + C) of the column's list, so that a key block listed by many query blocks
-// (a global block) is shared by several workgroups.  A column with one chunk
-// writes its bf16 rows directly; the chunks of a split column add their fp32
-// partials into `acc` (converted afterwards).
-template <int D, int BLK>
+// + C) of the column's list (C <= 64), so that a key block listed by many
+// query blocks (a global block) is shared by several workgroups.  A column with
+// one chunk writes its bf16 rows directly; the chunks of a split column add
+// their fp32 partials into `acc` (converted afterwards).
+//
+// The item's query blocks (and their q heads) are held in VGPR lanes; their
+// 64-row tiles of Q and dO, with the rows' {lse log2(e), D} pairs, are copied
+// global -> LDS by direct loads into a ring of S slots (tile n + S - 1 in
+// flight while tile n is used).  Each wave copies the row statistics it reads
+// into an area of its own.
+template <int D, int BLK, int S>
 __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
   using L = TileLds<D>;
-  constexpr int NU = D / 16, NT = D / 32, NTH = 2 * BLK;
+  constexpr int NW = BLK / 32, NU = D / 16, NT = D / 32, SUBS = BLK / 64;
+  using M = TileDma<D, NW>;
+  constexpr int SLOT = 2 * M::TB + NW * 1024;  // Q tile, dO tile, per-wave statistics
+  constexpr int CP = 2 * M::JN + 1;            // copies per wave per tile
+  static_assert(S == 2 || S == 3, "ring slots");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* qs = smem;
-  uint8_t* gs = smem + BLK * 2 * D;
-  float* ls = (float*)(smem + 2 * BLK * 2 * D);
-  float* dls = ls + BLK;
   const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
   const int32_t rep = a.H / a.H_kv;
   const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
   const int32_t items = a.pre[cols];
+  const uint32_t ring = sa::lds_addr(smem);
+  const uint32_t soff = 16u * (uint32_t)(lane & 31);  // statistics: 2 rows per lane, lanes 32.. repeat
+  bool first = true;
   for (int32_t item = blockIdx.x; item < items; item += gridDim.x) {
     // column of the item: the last c with pre[c] <= item
     int64_t lo = 0, hi = cols;
@@ -563,11 +686,12 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
     }
     const int64_t c = sa::uniform((int32_t)lo);
     const int32_t chunk = sa::uniform(item - a.pre[c]);
-    const bool split = a.pre[c + 1] - a.pre[c] > 1;
+    const int split = sa::uniform((int)(a.pre[c + 1] - a.pre[c] > 1));
     const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
     const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
-    const int32_t f0 = chunk * a.chunk, f1 = f0 + a.chunk;  // flat entry range of this item
-    const int64_t sk = (int64_t)j * BLK + 32 * w + (lane & 31);  // this lane's key (C column)
+    const int32_t f0 = chunk * a.chunk;  // first flat entry of this item
+    const int koff = 32 * w + (lane & 31);        // this lane's key inside the block
+    const int64_t sk = (int64_t)j * BLK + koff;   // ... and in the sequence (C column)
     const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
     const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
     sa::u32x4 kb_[NU], vb_[NU];  // B operands: column = key, k = d
@@ -576,65 +700,95 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
       kb_[u] = *(const sa::u32x4*)(K + sk * a.st[TK][2] + 16 * u + 8 * hl);
       vb_[u] = *(const sa::u32x4*)(V + sk * a.st[TV][2] + 16 * u + 8 * hl);
     }
+    // the item's entries: flat entry f0 + x (over the heads in order) in lane x
+    int32_t lq = -1, lh = 0, total = 0;
+    for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
+      int32_t e0, e1;
+      col_range(a, (int64_t)b * a.mbs + (int64_t)h * a.mhs, j, e0, e1);
+      const int32_t x = f0 + lane - total;
+      if (lane < a.chunk && x >= 0 && x < e1 - e0) {
+        const int32_t qb = a.row_idx[e0 + x];
+        lq = ((uint32_t)qb < (uint32_t)a.nb && !(a.causal && qb < j)) ? qb : -1;
+        lh = h;
+      }
+      total += e1 - e0;
+    }
+    const int cnt = sa::uniform(max(0, min(a.chunk, total - f0)));
+    // the loads above complete here, before any copy is in flight (stores of
+    // the previous item included)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) sa::keep(kb_[u]), sa::keep(vb_[u]);
+    sa::keep(lq), sa::keep(lh), sa::keep(split);
+    sa::vm_wait<0>();
+    if (!first) ring_barrier();  // every wave is done with the ring
+    first = false;
+
     sa::f32x16 dk[NT], dv[NT];
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) dk[dt] = sa::f32x16{}, dv[dt] = sa::f32x16{};
-    int32_t fbase = 0;  // flat index of the current head's first entry
-    for (int h = kvh * rep; h < (kvh + 1) * rep; ++h) {
-      const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+    const int T = cnt * SUBS;
+    auto issue = [&](int m) {
+      const int32_t qb = sa::readlane(lq, m / SUBS), h = sa::readlane(lh, m / SUBS);
+      const int64_t r0 = (int64_t)(qb < 0 ? j : qb) * BLK + 64 * (m % SUBS);
       const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
       const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
-      const int64_t rowb = ((int64_t)b * a.H + h) * a.N;
-      int32_t e0, e1;
-      col_range(a, g, j, e0, e1);
-      const int32_t lo_e = max(e0, e0 + f0 - fbase), hi_e = min(e1, e0 + f1 - fbase);
-      fbase += e1 - e0;
-      for (int32_t e = lo_e; e < hi_e; ++e) {
-        const int32_t qb = sa::uniform(a.row_idx[e]);
-        if (qb < 0 || qb >= a.nb || (a.causal && qb < j)) continue;
-        __syncthreads();
-        stage_rows<D>(qs, Q, (int64_t)qb * BLK, a.st[TQ][2], BLK, tid, NTH);
-        stage_rows<D>(gs, G, (int64_t)qb * BLK, a.st[TDO][2], BLK, tid, NTH);
-        for (int r = tid; r < BLK; r += NTH) {
-          ls[r] = lse2_of(a.lse[rowb + (int64_t)qb * BLK + r]);
-          dls[r] = a.delta[rowb + (int64_t)qb * BLK + r];
+      const float* st = (const float*)(a.stat + ((int64_t)b * a.H + h) * a.N + r0);
+      const uint32_t dst = ring + (m % S) * SLOT;
+      M::copy(Q + r0 * a.st[TQ][2], a.st[TQ][2], M::lane_off(w, lane, a.st[TQ][2]), dst, w);
+      M::copy(G + r0 * a.st[TDO][2], a.st[TDO][2], M::lane_off(w, lane, a.st[TDO][2]), dst + M::TB, w);
+      sa::dma16(st, soff, dst + 2 * M::TB + w * 1024);
+    };
+    if (T > 0) issue(0);
+    if (S > 2 && T > 1) issue(1);
+    for (int n = 0; n < T; ++n) {
+      wait_units<CP>(S > 2 && n + 1 < T);
+      ring_barrier();
+      if (n + S - 1 < T) issue(n + S - 1);
+      const int32_t qb = sa::readlane(lq, n / SUBS);
+      if (qb < 0) continue;
+      const uint8_t* qs = smem + (n % S) * SLOT;
+      const uint8_t* gs = qs + M::TB;
+      const float* sts = (const float*)(gs + M::TB + w * 1024);
+      const int qsub = 64 * (n % SUBS);
+      const bool diag = a.causal && qb == j;
+      // one 32-query half; MASK: apply the causal triangle when diag
+      auto half = [&](int qt, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        // S and dP [32 queries x 32 keys]
+        sa::f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
+          dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vb_[u], dp);
         }
-        __syncthreads();
-#pragma unroll 1
-        for (int qt = 0; qt < BLK / 32; ++qt) {
-          // S and dP [32 queries x 32 keys]
-          sa::f32x16 s = {}, dp = {};
+        float p[16], ds[16];
 #pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
-            dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vb_[u], dp);
-          }
-          float p[16], ds[16];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
+          const sa::f32x4 x0 = *(const sa::f32x4*)(sts + 2 * q4);  // {l, D} of rows q4, q4 + 1
+          const sa::f32x4 x1 = *(const sa::f32x4*)(sts + 2 * q4 + 4);
+          const float lv[4] = {x0[0], x0[2], x1[0], x1[2]}, dv4[4] = {x0[1], x0[3], x1[1], x1[3]};
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
-            const sa::f32x4 l4 = *(const sa::f32x4*)(ls + q4);
-            const sa::f32x4 d4 = *(const sa::f32x4*)(dls + q4);
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-              const int r = 4 * r4 + cc;
-              const int64_t tq = (int64_t)qb * BLK + q4 + cc;
-              p[r] = (a.causal && sk > tq) ? 0.f : exp2f(s[r] * a.c2 - l4[cc]);
-              ds[r] = p[r] * (dp[r] - d4[cc]);
-            }
-          }
-          // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
-#pragma unroll
-            for (int dt = 0; dt < NT; ++dt) {
-              dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
-              dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
-            }
+          for (int cc = 0; cc < 4; ++cc) {
+            const int r = 4 * r4 + cc;
+            p[r] = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -lv[cc]));
+            // keys after the query
+            if (MASK && diag && koff > qsub + q4 + cc) p[r] = 0.f;
+            ds[r] = p[r] * (dp[r] - dv4[cc]);
           }
         }
-      }
+        // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) {
+            dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
+            dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
+          }
+        }
+      };
+      bwd_tile<D>(diag, half);
     }
     // C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's key
     if (!split) {
@@ -941,22 +1095,37 @@ sa_status common_args(BwdArgs& a, int32_t dtype, const void* q, const void* k, c
   return SA_OK;
 }
 
-sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t stream) {
+sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, bool stat, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const int64_t blocks = (rows * (d / 8) + 255) / 256;
-  if (dtype == SA_BF16)
-    return d == 64 ? launch(delta_kernel<64, true>, a, blocks, 256, 0, stream, "delta_kernel")
-                   : launch(delta_kernel<128, true>, a, blocks, 256, 0, stream, "delta_kernel");
-  return d == 64 ? launch(delta_kernel<64, false>, a, blocks, 256, 0, stream, "delta_kernel")
-                 : launch(delta_kernel<128, false>, a, blocks, 256, 0, stream, "delta_kernel");
+  if (dtype == SA_BF16) {
+    if (stat)
+      return d == 64 ? launch(delta_kernel<64, true, true>, a, blocks, 256, 0, stream, "delta_kernel")
+                     : launch(delta_kernel<128, true, true>, a, blocks, 256, 0, stream, "delta_kernel");
+    return d == 64 ? launch(delta_kernel<64, true, false>, a, blocks, 256, 0, stream, "delta_kernel")
+                   : launch(delta_kernel<128, true, false>, a, blocks, 256, 0, stream, "delta_kernel");
+  }
+  return d == 64 ? launch(delta_kernel<64, false, false>, a, blocks, 256, 0, stream, "delta_kernel")
+                 : launch(delta_kernel<128, false, false>, a, blocks, 256, 0, stream, "delta_kernel");
 }
+
+// ring slots of the block-sparse bf16 dQ and dK/dV kernels
+#ifndef SA_BWD_DQ_SLOTS
+#define SA_BWD_DQ_SLOTS 2
+#endif
+#ifndef SA_BWD_DKDV_SLOTS
+#define SA_BWD_DKDV_SLOTS 2
+#endif
 
 template <int D, int BLK>
 sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
   const int64_t nq = (int64_t)a.B * a.H * a.nb, nk = (int64_t)a.B * a.H_kv * a.nb;
   sa_status st;
   if (bf16) {
-    st = launch(bsa_bwd_dq_bf16<D, BLK>, a, nq, 2 * BLK, 2 * BLK * 2 * D, stream, "bsa_bwd_dq_bf16");
+    constexpr int SQ = SA_BWD_DQ_SLOTS, SK = SA_BWD_DKDV_SLOTS;
+    constexpr int lds_dq = SQ * 2 * TileDma<D, BLK / 32>::TB;
+    constexpr int lds_kv = SK * (2 * TileDma<D, BLK / 32>::TB + BLK / 32 * 1024);
+    st = launch(bsa_bwd_dq_bf16<D, BLK, SQ>, a, nq, 2 * BLK, lds_dq, stream, "bsa_bwd_dq_bf16");
     if (st != SA_OK) return st;
     const int64_t wblocks = (nk + 3) / 4;
     st = launch(dkdv_plan_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_plan_kernel");
@@ -965,8 +1134,8 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     st = sa_host::check_launch("scan_kernel");
     if (st != SA_OK) return st;
     // persistent workgroups; the item count lives on the device
-    st = launch(bsa_bwd_dkdv_bf16<D, BLK>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK,
-                2 * BLK * 2 * D + 2 * BLK * 4, stream, "bsa_bwd_dkdv_bf16");
+    st = launch(bsa_bwd_dkdv_bf16<D, BLK, SK>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK, lds_kv,
+                stream, "bsa_bwd_dkdv_bf16");
     if (st != SA_OK) return st;
     return launch(dkdv_convert_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_convert_kernel");
   }
@@ -975,8 +1144,9 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
   return launch(bsa_bwd_dkdv_f32<D, BLK>, a, nk, BLK, 0, stream, "bsa_bwd_dkdv_f32");
 }
 
-// Workspace of sparse_attn_bwd: delta fp32 [B*H*N] | pre int32 [B*H_kv*nb + 1]
-// | acc fp32 [2][B*H_kv*N*d], each part 256-byte aligned.
+// Workspace of sparse_attn_bwd: row statistics fp32 [B*H*N][2] ({lse log2(e),
+// D} pairs; D alone in the first half for fp32) | pre int32 [B*H_kv*nb + 1] |
+// acc fp32 [2][B*H_kv*N*d], each part 256-byte aligned.
 struct WsLayout {
   int64_t delta, pre, acc, total;
 };
@@ -984,7 +1154,7 @@ WsLayout ws_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   WsLayout l;
   l.delta = 0;
-  l.pre = up(B * H * N * 4);
+  l.pre = up(B * H * N * 8);
   l.acc = l.pre + up((B * H_kv * (N / block) + 1) * 4);
   l.total = l.acc + up(2 * B * H_kv * N * d * 4);
   return l;
@@ -1037,6 +1207,7 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
   sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, (float*)(ws + wsl.delta), B, H, H_kv,
                              N, d, strides, scale);
   if (st != SA_OK) return st;
+  a.stat = (sa::f32x2*)(ws + wsl.delta);
   a.pre = (int32_t*)(ws + wsl.pre);
   a.acc = (float*)(ws + wsl.acc);
   a.chunk = 32;
@@ -1046,12 +1217,16 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
     return SA_ERR_INVALID;
   if (N % block != 0) return SA_ERR_INVALID;
   if (block != 64 && block != 128) return SA_ERR_UNSUPPORTED;
+  // the bf16 kernels keep the byte offsets of the rows of a 64-row tile in 32 bits
+  if (dtype == SA_BF16)
+    for (int t : {(int)TQ, (int)TK, (int)TV, (int)TDO})
+      if (a.st[t][2] >= (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
   a.row_ptr = row_ptr, a.col_idx = col_idx, a.col_ptr = col_ptr, a.row_idx = row_idx;
   a.col_capacity = col_capacity, a.row_capacity = row_capacity;
   a.nb = N / block, a.G = num_groups, a.mbs = mask_batch_stride, a.mhs = mask_head_stride, a.causal = causal;
-  st = launch_delta(a, dtype, d, stream);
-  if (st != SA_OK) return st;
   const bool bf = dtype == SA_BF16;
+  st = launch_delta(a, dtype, d, bf, stream);
+  if (st != SA_OK) return st;
   if (d == 64) return block == 64 ? launch_bsa_bwd<64, 64>(a, bf, stream) : launch_bsa_bwd<64, 128>(a, bf, stream);
   return block == 64 ? launch_bsa_bwd<128, 64>(a, bf, stream) : launch_bsa_bwd<128, 128>(a, bf, stream);
 }
@@ -1072,7 +1247,7 @@ extern "C" sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k
   }
   a.noff = num_offsets;
   for (int n = 0; n < num_offsets; ++n) a.offs[n] = offsets[n];
-  st = launch_delta(a, dtype, d, stream);
+  st = launch_delta(a, dtype, d, false, stream);
   if (st != SA_OK) return st;
   const int64_t tiles = ((int64_t)N + 255) / 256;
   const int64_t nq = (int64_t)B * H * tiles, nk = (int64_t)B * H_kv * tiles;

@@ -233,6 +233,11 @@ __device__ __forceinline__ void keep(int x) {
   asm volatile("" ::"v"(x));
 #endif
 }
+__device__ __forceinline__ void keep(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
 
 // Transpose read of 4 x 16-bit values: within each group of 16 lanes, lane i
 // receives element (i % 4) of the 8-byte words read by lanes i/4, i/4 + 4,
