@@ -647,9 +647,9 @@ __global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
 }
 
 // dk, dv: persistent workgroups (BLK/32 waves, a wave per 32 keys of the key
-// block) take work items w = chunk of column c: entries [chunk * C, chunk * C
-// + C) of the column's list (C <= 64), so that a key block listed by many
-// query blocks (a global block) is shared by several workgroups.  A column with
+// block) take work items = chunks of columns: entries [chunk * C, chunk * C +
+// C) of the column's list (C <= 64), so that a key block listed by many query
+// blocks (a global block) is shared by several workgroups.  A column with
 // one chunk writes its bf16 rows directly; the chunks of a split column add
 // their fp32 partials into `acc` (converted afterwards).
 //
@@ -671,21 +671,34 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
   const int32_t rep = a.H / a.H_kv;
   const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
   const int32_t items = a.pre[cols];
+  // Items [0, extra) are the second and later chunks of split columns (the
+  // long ones, started first); item extra + c is the first chunk of column c.
+  const int32_t extra = items - (int32_t)cols;
   const uint32_t ring = sa::lds_addr(smem);
   const uint32_t soff = 16u * (uint32_t)(lane & 31);  // statistics: 2 rows per lane, lanes 32.. repeat
   bool first = true;
   for (int32_t item = blockIdx.x; item < items; item += gridDim.x) {
-    // column of the item: the last c with pre[c] <= item
-    int64_t lo = 0, hi = cols;
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (a.pre[mid] <= item)
-        lo = mid;
-      else
-        hi = mid;
+    int64_t c;
+    int32_t chunk;
+    if (item >= extra) {
+      c = item - extra;
+      chunk = 0;
+    } else {
+      // pre[c] - c counts the extra chunks of the columns before c: the item's
+      // column is the last c with pre[c] - c <= item
+      int64_t lo = 0, hi = cols;
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (a.pre[mid] - mid <= item)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      c = lo;
+      chunk = 1 + item - (int32_t)(a.pre[c] - c);
     }
-    const int64_t c = sa::uniform((int32_t)lo);
-    const int32_t chunk = sa::uniform(item - a.pre[c]);
+    c = sa::uniform((int32_t)c);
+    chunk = sa::uniform(chunk);
     const int split = sa::uniform((int)(a.pre[c + 1] - a.pre[c] > 1));
     const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
     const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
