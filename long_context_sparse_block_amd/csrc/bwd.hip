@@ -1122,6 +1122,12 @@ sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, bool stat, hi
                  : launch(delta_kernel<128, false, false>, a, blocks, 256, 0, stream, "delta_kernel");
 }
 
+// 64-row tiles per dK/dV work item: longer columns are split over several
+// workgroups (an item's list of at most 64 entries is held in VGPR lanes)
+#ifndef SA_BWD_CHUNK_TILES
+#define SA_BWD_CHUNK_TILES 64
+#endif
+
 // ring slots of the block-sparse bf16 dQ and dK/dV kernels
 #ifndef SA_BWD_DQ_SLOTS
 #define SA_BWD_DQ_SLOTS 2
@@ -1223,7 +1229,7 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
   a.stat = (sa::f32x2*)(ws + wsl.delta);
   a.pre = (int32_t*)(ws + wsl.pre);
   a.acc = (float*)(ws + wsl.acc);
-  a.chunk = 32;
+  a.chunk = std::max(1, std::min(64, SA_BWD_CHUNK_TILES / std::max(1, block / 64)));  // CSR entries per item
   if (block < 1 || causal < 0 || causal > 1 || col_capacity < 0 || row_capacity < 0) return SA_ERR_INVALID;
   if (num_groups < 1 || mask_batch_stride < 0 || mask_head_stride < 0) return SA_ERR_INVALID;
   if ((int64_t)(B - 1) * mask_batch_stride + (int64_t)(H - 1) * mask_head_stride >= num_groups)
