@@ -334,13 +334,16 @@ sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, con
  *   dq [B, H, N, d], dk, dv [B, H_kv, N, d]  DEVICE, written (input dtype)
  *   workspace        DEVICE, 16-byte aligned, workspace_bytes >=
  *                    sparse_attn_bwd_workspace_bytes(B, H, H_kv, N, d, block)
- *                    (else SA_ERR_CAPACITY): D, the dK/dV work list, and fp32
- *                    partial dK/dV of key blocks listed by more than 32 query
- *                    blocks (those are split over several workgroups and their
+ *                    (else SA_ERR_CAPACITY): per-row {lse log2(e), D}, the
+ *                    dK/dV work list, and fp32 partial dK/dV of key blocks
+ *                    listed by more than 64 query blocks (32 at block 128);
+ *                    those are split over several workgroups and their
  *                    partial sums added with fp32 atomics, so their low-order
- *                    bits may differ from run to run)
+ *                    bits may differ from run to run
  *   strides          HOST int64 [8][3] for q, k, v, o, dout, dq, dk, dv
- *                    (batch, head, sequence strides in elements) or NULL
+ *                    (batch, head, sequence strides in elements) or NULL; for
+ *                    bf16 the sequence strides of q, k, v, dout must be below
+ *                    2^24 elements (else SA_ERR_UNSUPPORTED)
  * Other arguments, layouts, supported sizes and errors as for sparse_attn_fwd.
  */
 int64_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
