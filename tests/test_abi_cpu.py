@@ -232,3 +232,48 @@ def test_offset_interp_split_matches_oracle(lib):
     cnt, rc = ctypes.c_int32(), ctypes.c_int32()
     assert lib.offset_attn_make_interp(1, 1.5, b, 2, 100, out, 8, ctypes.byref(cnt), rf, rw, 1,
                                        ctypes.byref(rc)) == L.SA_ERR_CAPACITY
+
+
+def _bwd(lib, **kw):
+    fake = ctypes.c_void_p(1 << 20)
+    a = dict(dtype=L.SA_BF16, ws=fake, ws_bytes=1 << 40, B=1, H=2, H_kv=2, N=512, d=64, block=64,
+             strides=None, G=1, mbs=0, mhs=0, causal=1, scale=0.125)
+    a.update(kw)
+    return lib.sparse_attn_bwd(a["dtype"], fake, fake, fake, fake, fake, fake, fake, fake, fake, a["ws"],
+                               a["ws_bytes"], a["B"], a["H"], a["H_kv"], a["N"], a["d"], a["block"],
+                               a["strides"], fake, fake, 100, fake, fake, 100, a["G"], a["mbs"], a["mhs"],
+                               a["causal"], a["scale"], None)
+
+
+def _bwd_strides(seq_q):
+    """Per-tensor (batch, head, sequence) strides of q, k, v, o, dout, dq, dk, dv."""
+    s = []
+    for t in range(8):
+        ss = seq_q if t == 0 else 64
+        s += [2 * 512 * ss, 512 * ss, ss]
+    return (ctypes.c_int64 * 24)(*s)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ws=None), L.SA_ERR_NULL),
+    (dict(ws_bytes=0), L.SA_ERR_CAPACITY),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 4)), L.SA_ERR_INVALID),  # misaligned workspace
+    (dict(d=96), L.SA_ERR_UNSUPPORTED),
+    (dict(block=32), L.SA_ERR_UNSUPPORTED),
+    (dict(N=500), L.SA_ERR_INVALID),
+    (dict(causal=2), L.SA_ERR_INVALID),
+    (dict(G=1, mhs=1), L.SA_ERR_INVALID),
+    # bf16: row byte offsets of a 64-row tile are kept in 32 bits
+    (dict(strides=_bwd_strides(1 << 24)), L.SA_ERR_UNSUPPORTED),
+])
+def test_bwd_host_errors(lib, over, status):
+    assert _bwd(lib, **over) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    # {lse log2(e), D} per row | work-item prefix | fp32 partial dK, dV; parts 256-byte aligned
+    up = lambda x: (x + 255) // 256 * 256
+    for B, H, Hkv, N, d, blk in ((1, 2, 2, 512, 64, 64), (2, 8, 2, 4096, 128, 128), (3, 3, 1, 192, 64, 64)):
+        want = up(8 * B * H * N) + up(4 * (B * Hkv * (N // blk) + 1)) + up(2 * 4 * B * Hkv * N * d)
+        assert lib.sparse_attn_bwd_workspace_bytes(B, H, Hkv, N, d, blk) == want
+    assert lib.sparse_attn_bwd_workspace_bytes(0, 1, 1, 64, 64, 64) < 0
