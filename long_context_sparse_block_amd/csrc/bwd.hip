@@ -646,8 +646,20 @@ __global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
   }
 }
 
-// dk, dv: persistent workgroups (BLK/32 waves, a wave per 32 keys of the key
-// block) take work items = chunks of columns: entries [chunk * C, chunk * C +
+// d = 128: SA_BWD_DKDV_DSPLIT waves per 32 keys, each recomputing S and dP and
+// holding 1 / DSPLIT of the dK, dV accumulators.  The full set needs more than
+// 256 registers (one wave per SIMD); two waves per SIMD with the split measured
+// slower on the long-context workload (7.04 vs 6.71 ms), so the default is 1.
+#ifndef SA_BWD_DKDV_DSPLIT
+#define SA_BWD_DKDV_DSPLIT 1
+#endif
+template <int D>
+struct DkdvCfg {
+  static constexpr int DS = D == 128 ? SA_BWD_DKDV_DSPLIT : 1;
+};
+
+// dk, dv: persistent workgroups (BLK/32 * DS waves, DS waves per 32 keys of
+// the key block) take work items = chunks of columns: entries [chunk * C, chunk * C +
 // C) of the column's list (C <= 64), so that a key block listed by many query
 // blocks (a global block) is shared by several workgroups.  A column with
 // one chunk writes its bf16 rows directly; the chunks of a split column add
@@ -656,18 +668,20 @@ __global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
 // The item's query blocks (and their q heads) are held in VGPR lanes; their
 // 64-row tiles of Q and dO, with the rows' {lse log2(e), D} pairs, are copied
 // global -> LDS by direct loads into a ring of S slots (tile n + S - 1 in
-// flight while tile n is used).  Each wave copies the row statistics it reads
-// into an area of its own.
+// flight while tile n is used).  Wave 0 copies the tile's row statistics,
+// which every wave reads after the ring barrier.
 template <int D, int BLK, int S>
-__global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
+__global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(BwdArgs a) {
   using L = TileLds<D>;
-  constexpr int NW = BLK / 32, NU = D / 16, NT = D / 32, SUBS = BLK / 64;
+  constexpr int DS = DkdvCfg<D>::DS;  // waves per 32 keys, each holding NT / DS of the dK, dV tiles
+  constexpr int NW = BLK / 32 * DS, NU = D / 16, NT = D / 32, NTW = NT / DS, SUBS = BLK / 64;
   using M = TileDma<D, NW>;
-  constexpr int SLOT = 2 * M::TB + NW * 1024;  // Q tile, dO tile, per-wave statistics
-  constexpr int CP = 2 * M::JN + 1;            // copies per wave per tile
+  constexpr int SLOT = 2 * M::TB + 1024;  // Q tile, dO tile, the rows' statistics
+  constexpr int CP = 2 * M::JN;           // tile copies per wave per tile (wave 0: + 1)
   static_assert(S == 2 || S == 3, "ring slots");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
+  const int kg = w / DS, dh = w % DS;  // key group (32 keys) and d part of this wave
   const int32_t rep = a.H / a.H_kv;
   const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
   const int32_t items = a.pre[cols];
@@ -703,7 +717,7 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
     const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
     const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
     const int32_t f0 = chunk * a.chunk;  // first flat entry of this item
-    const int koff = 32 * w + (lane & 31);        // this lane's key inside the block
+    const int koff = 32 * kg + (lane & 31);       // this lane's key inside the block
     const int64_t sk = (int64_t)j * BLK + koff;   // ... and in the sequence (C column)
     const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
     const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
@@ -736,9 +750,9 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
     if (!first) ring_barrier();  // every wave is done with the ring
     first = false;
 
-    sa::f32x16 dk[NT], dv[NT];
+    sa::f32x16 dk[NTW], dv[NTW];  // d tiles dh NTW + t
 #pragma unroll
-    for (int dt = 0; dt < NT; ++dt) dk[dt] = sa::f32x16{}, dv[dt] = sa::f32x16{};
+    for (int t = 0; t < NTW; ++t) dk[t] = sa::f32x16{}, dv[t] = sa::f32x16{};
     const int T = cnt * SUBS;
     auto issue = [&](int m) {
       const int32_t qb = sa::readlane(lq, m / SUBS), h = sa::readlane(lh, m / SUBS);
@@ -749,19 +763,22 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
       const uint32_t dst = ring + (m % S) * SLOT;
       M::copy(Q + r0 * a.st[TQ][2], a.st[TQ][2], M::lane_off(w, lane, a.st[TQ][2]), dst, w);
       M::copy(G + r0 * a.st[TDO][2], a.st[TDO][2], M::lane_off(w, lane, a.st[TDO][2]), dst + M::TB, w);
-      sa::dma16(st, soff, dst + 2 * M::TB + w * 1024);
+      if (w == 0) sa::dma16(st, soff, dst + 2 * M::TB);
     };
     if (T > 0) issue(0);
     if (S > 2 && T > 1) issue(1);
     for (int n = 0; n < T; ++n) {
-      wait_units<CP>(S > 2 && n + 1 < T);
+      if (w == 0)
+        wait_units<CP + 1>(S > 2 && n + 1 < T);
+      else
+        wait_units<CP>(S > 2 && n + 1 < T);
       ring_barrier();
       if (n + S - 1 < T) issue(n + S - 1);
       const int32_t qb = sa::readlane(lq, n / SUBS);
       if (qb < 0) continue;
       const uint8_t* qs = smem + (n % S) * SLOT;
       const uint8_t* gs = qs + M::TB;
-      const float* sts = (const float*)(gs + M::TB + w * 1024);
+      const float* sts = (const float*)(gs + M::TB);
       const int qsub = 64 * (n % SUBS);
       const bool diag = a.causal && qb == j;
       // one 32-query half; MASK: apply the causal triangle when diag
@@ -795,9 +812,10 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
         for (int st = 0; st < 2; ++st) {
           const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
 #pragma unroll
-          for (int dt = 0; dt < NT; ++dt) {
-            dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
-            dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
+          for (int t = 0; t < NTW; ++t) {
+            const int dt = dh * NTW + t;
+            dv[t] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[t]);
+            dk[t] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[t]);
           }
         }
       };
@@ -808,11 +826,12 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
       uint16_t* DK = (uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + sk * a.st[TDK][2];
       uint16_t* DV = (uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + sk * a.st[TDV][2];
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const sa::f32x16& x = dk[dt];
-          const sa::f32x16& y = dv[dt];
+          const int dt = dh * NTW + t;
+          const sa::f32x16& x = dk[t];
+          const sa::f32x16& y = dv[t];
           const int r = 4 * r4;
           *(sa::u32x2*)(DK + 32 * dt + 8 * r4 + 4 * hl) = sa::u32x2{
               sa::pack_bf16x2(x[r] * a.scale, x[r + 1] * a.scale), sa::pack_bf16x2(x[r + 2] * a.scale, x[r + 3] * a.scale)};
@@ -823,12 +842,12 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dkdv_bf16(BwdArgs a) {
       const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
       float* pk = a.acc + ((int64_t)bk * a.N + sk) * D;
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int x = 32 * dt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          atomicAdd(pk + x, dk[dt][r]);
-          atomicAdd(pk + plane + x, dv[dt][r]);
+          const int x = 32 * (dh * NTW + t) + 8 * (r >> 2) + 4 * hl + (r & 3);
+          atomicAdd(pk + x, dk[t][r]);
+          atomicAdd(pk + plane + x, dv[t][r]);
         }
     }
   }
@@ -1143,7 +1162,8 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
   if (bf16) {
     constexpr int SQ = SA_BWD_DQ_SLOTS, SK = SA_BWD_DKDV_SLOTS;
     constexpr int lds_dq = SQ * 2 * TileDma<D, BLK / 32>::TB;
-    constexpr int lds_kv = SK * (2 * TileDma<D, BLK / 32>::TB + BLK / 32 * 1024);
+    constexpr int DS = DkdvCfg<D>::DS;
+    constexpr int lds_kv = SK * (2 * TileDma<D, BLK / 32 * DS>::TB + 1024);
     st = launch(bsa_bwd_dq_bf16<D, BLK, SQ>, a, nq, 2 * BLK, lds_dq, stream, "bsa_bwd_dq_bf16");
     if (st != SA_OK) return st;
     const int64_t wblocks = (nk + 3) / 4;
@@ -1153,7 +1173,7 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     st = sa_host::check_launch("scan_kernel");
     if (st != SA_OK) return st;
     // persistent workgroups; the item count lives on the device
-    st = launch(bsa_bwd_dkdv_bf16<D, BLK, SK>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK, lds_kv,
+    st = launch(bsa_bwd_dkdv_bf16<D, BLK, SK>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK * DS, lds_kv,
                 stream, "bsa_bwd_dkdv_bf16");
     if (st != SA_OK) return st;
     return launch(dkdv_convert_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_convert_kernel");
