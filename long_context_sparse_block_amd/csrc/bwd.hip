@@ -5,16 +5,18 @@
 //     dQ = scale dS K,   dK = scale dS^T Q
 // (masked pairs contribute nothing; grouped-query heads add into their K/V
 // head).  Kernels:
-//   * delta: D = rowsum(dO * O), fp32;
+//   * delta: D = rowsum(dO * O), fp32 (for the block-sparse bf16 kernels
+//     stored with lse log2(e) as one pair per row);
 //   * mask transpose: the CSR key-block lists -> per key block the ascending
 //     list of query blocks that list it (CSC), one wave per column;
 //   * block-sparse bf16: a dQ kernel over the CSR rows (one workgroup per
 //     query block, a wave per 32 queries, S^T = K Q^T so each lane owns a
-//     query) and a dK/dV kernel over the CSC columns (one workgroup per key
-//     block, a wave per 32 keys, S = Q K^T so each lane owns a key); all five
-//     products on v_mfma_f32_32x32x16_bf16, P and dS fed from the
+//     query) and a dK/dV kernel over chunks of the CSC columns (persistent
+//     workgroups, a wave per 32 keys, S = Q K^T so each lane owns a key); all
+//     five products on v_mfma_f32_32x32x16_bf16, P and dS fed from the
 //     accumulators as B operands, the transposed A operands (K^T, Q^T, dO^T)
-//     by ds_read_b64_tr_b16 from LDS;
+//     by ds_read_b64_tr_b16 from LDS, the 64-row tiles staged by direct
+//     global -> LDS copies into two-slot rings;
 //   * offsets bf16: four adjacent lanes per row (coalesced 64-byte segments),
 //     16 rows per wave, distances four at a time;
 //   * block-sparse fp32 and offsets fp32: one thread per row, plain fp32
@@ -1187,12 +1189,12 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
 // D} pairs; D alone in the first half for fp32) | pre int32 [B*H_kv*nb + 1] |
 // acc fp32 [2][B*H_kv*N*d], each part 256-byte aligned.
 struct WsLayout {
-  int64_t delta, pre, acc, total;
+  int64_t stat, pre, acc, total;
 };
 WsLayout ws_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int64_t block) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   WsLayout l;
-  l.delta = 0;
+  l.stat = 0;
   l.pre = up(B * H * N * 8);
   l.acc = l.pre + up((B * H_kv * (N / block) + 1) * 4);
   l.total = l.acc + up(2 * B * H_kv * N * d * 4);
@@ -1243,10 +1245,10 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
                                  d > 0 ? d : 1, block);
   if (workspace_bytes < wsl.total) return SA_ERR_CAPACITY;
   uint8_t* ws = (uint8_t*)workspace;
-  sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, (float*)(ws + wsl.delta), B, H, H_kv,
+  sa_status st = common_args(a, dtype, q, k, v, o, lse, dout, dq, dk, dv, (float*)(ws + wsl.stat), B, H, H_kv,
                              N, d, strides, scale);
   if (st != SA_OK) return st;
-  a.stat = (sa::f32x2*)(ws + wsl.delta);
+  a.stat = (sa::f32x2*)(ws + wsl.stat);
   a.pre = (int32_t*)(ws + wsl.pre);
   a.acc = (float*)(ws + wsl.acc);
   a.chunk = std::max(1, std::min(64, SA_BWD_CHUNK_TILES / std::max(1, block / 64)));  // CSR entries per item
