@@ -206,3 +206,61 @@ def test_offset_bwd_workload_reduced_batch():
         got, ref = _off_case(offs, 1, 2, 2, N, ow["d"], torch.bfloat16, ow["qkv_seed_base"][N] + 7,
                              1 / math.sqrt(ow["d"]))
         _check_all(got, ref, torch.bfloat16, f"offsets workload N={N}")
+
+
+def _hand_mask(rows, nb, causal):
+    row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    col_idx = np.array([c for r in rows for c in r] or [0], dtype=np.int32)
+    return api.BlockMask(torch.from_numpy(row_ptr).cuda(), torch.from_numpy(col_idx).cuda(), None, 1, nb,
+                         causal), row_ptr, col_idx[:row_ptr[-1]]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_bsa_bwd_hand_masks_empty_and_ignored(dtype):
+    """Empty rows and empty columns give zero gradients; entries out of range or
+    (causal) after the query block are skipped: the gradients equal those of
+    the clean mask bit for bit, and the oracle's for it."""
+    require_gpu()
+    nb, block, d, scale = 6, 64, 64, 0.125
+    rows_ok = [[], [0, 1, 3, 5], [2], [], [0, 4], [1, 2, 4, 5]]
+    rows_bad = [[-2], [0, 1, 3, 5, 9], [2, 4], [], [0, 4, 5], [1, 2, 4, 5, 77]]
+    for causal in (True, False):
+        announce(f"[bwd] hand masks causal={causal} {dtype}")
+        # non-causal: every in-range entry counts, only the out-of-range ones go
+        bad = rows_bad
+        ok = rows_ok if causal else [[c for c in r if 0 <= c < nb] for r in rows_bad]
+        q, k, v = wl.make_qkv(1, 2, nb * block, d, dtype, 95)
+        do = _dout(q.shape, dtype, 96)
+        qd, kd, vd, dod = [t.cuda() for t in (q, k, v, do)]
+        grads = []
+        for rows in (bad, ok):
+            mask, rp, ci = _hand_mask(rows, nb, causal)
+            o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, scale)
+            grads.append(api.sparse_attn_bwd(qd, kd, vd, o, lse, dod, mask, None, scale))
+        torch.cuda.synchronize()
+        for x, y, n in zip(grads[0], grads[1], ("dq", "dk", "dv")):
+            assert torch.equal(x, y), f"{n}: skipped entries changed the result"
+        _, rp, ci = _hand_mask(ok, nb, causal)
+        (gq, gk, gv), mags = ob.csr_attention_bwd(f64(q), f64(k), f64(v), f64(do), rp, ci, block, causal, scale,
+                                                   mags=True)
+        _check_all(grads[1], ((gq, gk, gv), mags), dtype, f"hand causal={causal}")
+        # query block 3 lists nothing: its dq rows are zero; key block 3 is listed
+        # by no usable row when causal
+        assert torch.count_nonzero(grads[1][0][:, :, 3 * block:4 * block]) == 0
+        if causal:
+            assert torch.count_nonzero(grads[1][1][:, :, 3 * block:4 * block]) == 0
+
+
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 1)])
+def test_bsa_bwd_bf16_split_columns_block64(H, Hkv):
+    """Key block 0 is global: listed by all 70 query blocks (of every q head of a
+    K/V head), more than one work item holds at block 64, so its dK / dV rows
+    are summed from several workgroups' fp32 partials."""
+    require_gpu()
+    nb, block, d = 70, 64, 64
+    spec = dict(num_blocks=nb, num_groups=1, causal=True, win_before=1, win_after=0, win_clamp=False,
+                global_blocks=[0], num_random=0, random_blocks=None, literal_mode="none", literal_flags=None,
+                literal_p=0.0, seed=0, mask_batch_stride=0, mask_head_stride=0)
+    announce(f"[bwd] split columns H={H} Hkv={Hkv}")
+    got, ref = _bsa_case(spec, 1, H, Hkv, nb * block, d, torch.bfloat16, 97)
+    _check_all(got, ref, torch.bfloat16, f"split columns H={H} Hkv={Hkv}")
