@@ -214,6 +214,13 @@ sa_status sparse_attn_literal_flags(const uint8_t* bytes, int32_t G, int64_t n_b
  *   num_groups G; (B-1)*mask_batch_stride + (H-1)*mask_head_stride < G,
  *              strides >= 0.
  *   scale      logit scale, e.g. 1/sqrt(d) (any finite value, 0 and < 0 included)
+ *   row_split  1 or 2 (else SA_ERR_INVALID): wave groups sharing one mask row
+ *              in the bf16 path.  2 splits every row's key tiles over two
+ *              groups whose softmax states are merged at the end: shorter
+ *              critical path when a few rows are much longer than the rest
+ *              (global rows of a non-causal mask), more waves per row
+ *              otherwise.  Same results up to fp32 summation order; the fp32
+ *              path ignores it.
  *   SA_ERR_UNSUPPORTED for bf16 when a K or V sequence stride is >= 2^24
  *              elements.
  */
@@ -222,7 +229,7 @@ sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const voi
                           int32_t block, const int64_t* strides, const int32_t* row_ptr,
                           const int32_t* col_idx, int64_t col_capacity, const int32_t* sched,
                           int32_t num_groups, int64_t mask_batch_stride, int64_t mask_head_stride,
-                          int32_t causal, float scale, hipStream_t stream);
+                          int32_t causal, float scale, int32_t row_split, hipStream_t stream);
 
 /*
  * Offset table of "Depth-Staggered Fibonacci Spacing for Sparse Attention",

@@ -1,8 +1,9 @@
 """MI355X (gfx950) sparse block / offset attention: HIP kernels behind a C ABI.
 
-The library (lib/libsparse_attn.so, built by ``build.py``) exports
-sparse_attn_build_mask, sparse_attn_fwd, offset_attn_fwd and offset_attn_fwd_interp; ``api`` binds them
-for PyTorch tensors.  ``workloads`` holds the seeded synthetic inputs.
+The library (lib/libsparse_attn.so, built by ``build.py``) exports the mask
+builder, the block-sparse and offset forwards and their backward passes (see
+include/sparse_attn.h); ``api`` binds them for PyTorch tensors.  ``workloads``
+holds the seeded synthetic inputs.
 """
 
 from .api import (  # noqa: F401
@@ -19,6 +20,7 @@ from .api import (  # noqa: F401
     offset_attn_make_table,
     offset_attn_make_table_ratio,
     power2_base,
+    row_split_for,
     sparse_attn_bwd,
     sparse_attn_build_mask,
     sparse_attn_check_mask_desc,

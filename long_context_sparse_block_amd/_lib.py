@@ -70,7 +70,7 @@ SIGNATURES = {
     "sparse_attn_build_mask": (_i32, [ctypes.POINTER(MaskDesc), _p, _p, _i64, _p, _p]),
     "sparse_attn_fwd": (_i32, [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(_i64), _p, _p, _i64, _p, _i32, _i64, _i64, _i32,
-                               _f32, _p]),
+                               _f32, _i32, _p]),
     "sparse_attn_literal_flags": (_i32, [_p, _i32, _i64, _i32, _i32, _p, _p]),
     "offset_attn_make_table": (_i32, [_i32, _f64, ctypes.POINTER(_i64), _i32, _i32,
                                       ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),

@@ -207,9 +207,17 @@ def _strides(*ts):
     return (ctypes.c_int64 * len(vals))(*vals)
 
 
+def row_split_for(spec):
+    """Wave groups per mask row for the bf16 forward: 2 when the spec has global
+    blocks and is not causal (its global rows then list every block, far more
+    than the other rows, and would otherwise bound the launch), else 1."""
+    return 2 if (not spec.get("causal", True)) and len(spec.get("global_blocks") or []) > 0 else 1
+
+
 def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_stride=0,
-                    use_schedule=True, out=None, lse=None):
-    """Block-sparse attention; returns (o, lse).  ``mask`` is a BlockMask."""
+                    use_schedule=True, out=None, lse=None, row_split=1):
+    """Block-sparse attention; returns (o, lse).  ``mask`` is a BlockMask;
+    ``row_split`` (1 or 2) as for the C entry point (see row_split_for)."""
     B, H, Hkv, N, d = _check_qkv(q, k, v)
     if N % mask.num_blocks:
         raise ValueError("N must be a multiple of the number of mask blocks")
@@ -222,7 +230,7 @@ def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_st
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, block,
         _strides(q, k, v, o), _ptr(mask.row_ptr), _ptr(mask.col_idx), mask.col_idx.numel(),
         _ptr(sched), mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal),
-        scale, _stream(q.device))
+        scale, int(row_split), _stream(q.device))
     _check(st, "sparse_attn_fwd")
     return o, lse_t
 
@@ -420,9 +428,10 @@ class BlockSparsePlan:
 
     ``build_mask()`` and ``forward()`` each make one C call and allocate
     nothing; outputs land in ``self.mask``, ``self.o`` and ``self.lse``.
+    ``row_split`` defaults to ``row_split_for(spec)``.
     """
 
-    def __init__(self, spec, q, k, v, scale=None, use_schedule=True):
+    def __init__(self, spec, q, k, v, scale=None, use_schedule=True, row_split=None):
         B, H, Hkv, N, d = _check_qkv(q, k, v)
         self.device = q.device
         self._keep = []
@@ -446,7 +455,8 @@ class BlockSparsePlan:
         self._fwd_args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(self.o), _ptr(self.lse), B, H,
                           Hkv, N, d, N // nb, _strides(q, k, v, self.o), _ptr(self.mask.row_ptr),
                           _ptr(self.mask.col_idx), self.mask.col_idx.numel(), _ptr(self.mask.sched),
-                          G, self.mbs, self.mhs, int(self._desc.causal), self.scale)
+                          G, self.mbs, self.mhs, int(self._desc.causal), self.scale,
+                          row_split_for(spec) if row_split is None else int(row_split))
         self._mask_args = (ctypes.byref(self._desc), _ptr(self.mask.row_ptr), _ptr(self.mask.col_idx),
                            self.mask.col_idx.numel(), _ptr(self.mask.sched))
         self._lib = L.lib()

@@ -661,6 +661,19 @@ sa_status launch(Kern kern, const BsaArgs& a, int threads, int lds_bytes, hipStr
 #ifndef SA_CFG_128_128
 #define SA_CFG_128_128 1, 2, false
 #endif
+// ... and with each row split over two wave groups (row_split = 2)
+#ifndef SA_CFG2_64_64
+#define SA_CFG2_64_64 2, 2, true
+#endif
+#ifndef SA_CFG2_64_128
+#define SA_CFG2_64_128 2, 2, true
+#endif
+#ifndef SA_CFG2_128_64
+#define SA_CFG2_128_64 2, 2, false
+#endif
+#ifndef SA_CFG2_128_128
+#define SA_CFG2_128_128 2, 2, false
+#endif
 
 // The kernel must be named in a non-template context for its host stub to be
 // emitted, hence a macro rather than a function template.
@@ -691,8 +704,9 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
                                      const int32_t* row_ptr, const int32_t* col_idx,
                                      int64_t col_capacity, const int32_t* sched, int32_t num_groups,
                                      int64_t mask_batch_stride, int64_t mask_head_stride,
-                                     int32_t causal, float scale, hipStream_t stream) {
+                                     int32_t causal, float scale, int32_t row_split, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !row_ptr || !col_idx) return SA_ERR_NULL;
+  if (row_split != 1 && row_split != 2) return SA_ERR_INVALID;
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_INVALID;
   if (B < 1 || H < 1 || H_kv < 1 || N < 1 || d < 1 || block < 1) return SA_ERR_INVALID;
   if (H % H_kv != 0) return SA_ERR_INVALID;
@@ -730,6 +744,12 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   a.scale_log2 = scale != 0.f ? fabsf(scale) * sa::kLog2e : 1e-30f;
   a.qsign = scale < 0.f ? 0x80008000u : 0u;
 
+  if (dtype == SA_BF16 && row_split == 2) {
+    if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG2_64_64, "bsa_fwd_bf16<64,64,split>");
+    if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG2_64_128, "bsa_fwd_bf16<64,128,split>");
+    if (d == 128 && block == 64) SA_LAUNCH_BF16(128, 64, SA_CFG2_128_64, "bsa_fwd_bf16<128,64,split>");
+    SA_LAUNCH_BF16(128, 128, SA_CFG2_128_128, "bsa_fwd_bf16<128,128,split>");
+  }
   if (dtype == SA_BF16) {
     if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG_64_64, "bsa_fwd_bf16<64,64>");
     if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG_64_128, "bsa_fwd_bf16<64,128>");

@@ -102,12 +102,12 @@ def _fwd(lib, **kw):
     fake = ctypes.c_void_p(1 << 20)
     a = dict(dtype=L.SA_BF16, q=fake, k=fake, v=fake, o=fake, lse=fake, B=1, H=2, H_kv=2, N=512,
              d=64, block=64, strides=None, row_ptr=fake, col_idx=fake, cap=100, sched=None, G=1,
-             mbs=0, mhs=0, causal=1, scale=0.125)
+             mbs=0, mhs=0, causal=1, scale=0.125, row_split=1)
     a.update(kw)
     return lib.sparse_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
                                a["H_kv"], a["N"], a["d"], a["block"], a["strides"], a["row_ptr"],
                                a["col_idx"], a["cap"], a["sched"], a["G"], a["mbs"], a["mhs"],
-                               a["causal"], a["scale"], None)
+                               a["causal"], a["scale"], a["row_split"], None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -121,6 +121,8 @@ def _fwd(lib, **kw):
     (dict(G=1, mhs=1), L.SA_ERR_INVALID),            # head group index out of range
     (dict(causal=2), L.SA_ERR_INVALID),
     (dict(scale=float("nan")), L.SA_ERR_INVALID),
+    (dict(row_split=0), L.SA_ERR_INVALID),
+    (dict(row_split=3), L.SA_ERR_INVALID),
     (dict(cap=-1), L.SA_ERR_INVALID),
     (dict(q=ctypes.c_void_p((1 << 20) + 2)), L.SA_ERR_INVALID),  # misaligned
     (dict(strides=(ctypes.c_int64 * 12)(*([8192 * 64, 8192 * 64, 60] * 4))), L.SA_ERR_INVALID),
@@ -277,3 +279,15 @@ def test_bwd_workspace_bytes(lib):
         want = up(8 * B * H * N) + up(4 * (B * Hkv * (N // blk) + 1)) + up(2 * 4 * B * Hkv * N * d)
         assert lib.sparse_attn_bwd_workspace_bytes(B, H, Hkv, N, d, blk) == want
     assert lib.sparse_attn_bwd_workspace_bytes(0, 1, 1, 64, 64, 64) < 0
+
+
+def test_plan_picks_row_split():
+    """Rows are split over two wave groups for non-causal masks with global
+    blocks only (their global rows list every block)."""
+    from long_context_sparse_block_amd import api
+    from long_context_sparse_block_amd import workloads as wl
+    assert api.row_split_for(wl.mask_spec(wl.BLOCK_WORKLOADS["bigbird"])) == 2
+    for name in ("compression-guided", "long-context", "gzip-guided", "tiny-fp32"):
+        assert api.row_split_for(wl.mask_spec(wl.BLOCK_WORKLOADS[name])) == 1
+    assert api.row_split_for(api.mask_preset("longformer", 64, causal=False)) == 2
+    assert api.row_split_for(api.mask_preset("local-only", 64, causal=False)) == 1

@@ -18,7 +18,7 @@ from tests.gpu_util import announce, compare, f64, require_gpu, workload_spec
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, spec, B=None, H=None, samples=None, use_schedule=True, seed=None):
+def _run(w, spec, B=None, H=None, samples=None, use_schedule=True, seed=None, row_split=1):
     """Run the GPU path for workload dict w (optionally fewer batch / heads) and
     compare against the oracle (all rows, or the given samples)."""
     B = w["B"] if B is None else B
@@ -29,7 +29,8 @@ def _run(w, spec, B=None, H=None, samples=None, use_schedule=True, seed=None):
     mask = api.sparse_attn_build_mask(spec)
     scale = 1.0 / math.sqrt(w["d"])
     mbs, mhs = spec["mask_batch_stride"], spec["mask_head_stride"]
-    o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, scale, mbs, mhs, use_schedule=use_schedule)
+    o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, scale, mbs, mhs, use_schedule=use_schedule,
+                                 row_split=row_split)
     torch.cuda.synchronize()
     rp, ci, _ = bm.build(spec)
     q64, k64, v64 = f64(q), f64(k), f64(v)
@@ -227,3 +228,42 @@ def test_unreferenced_blocks_poisoned():
         torch.cuda.synchronize()
         sl = slice(row * 64, (row + 1) * 64)
         assert torch.equal(o1[:, :, sl], o2[:, :, sl]) and torch.equal(l1[:, :, sl], l2[:, :, sl])
+
+
+@pytest.mark.parametrize("name,B,H", [("bigbird", 2, 3), ("compression-guided", 2, 2), ("gzip-head-groups", 1, 12)])
+def test_row_split_reduced_full_parity(name, B, H):
+    """Every row's tiles split over two wave groups, merged at the end."""
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS[name], name=name + "/split")
+    announce(f"[bsa] row split {name} B={B} H={H}")
+    _run(w, workload_spec(dict(w, B=B, H=H)), B=B, H=H, row_split=2)
+
+
+@pytest.mark.parametrize("d,block", [(64, 128), (128, 64), (128, 128)])
+def test_row_split_other_tile_shapes(d, block):
+    require_gpu()
+    for causal in (True, False):
+        w = dict(B=2, H=2, N=1024, d=d, block=block, dtype="bf16", causal=causal, win_before=1,
+                 win_after=0 if causal else 1, win_clamp=False, global_blocks=[0], num_random=2,
+                 literal_mode="pair", literal_p=0.3, mask_seed=13, groups="per-sequence", qkv_seed=79,
+                 name=f"split d{d}b{block} causal={causal}")
+        announce(f"[bsa] row split d={d} block={block} causal={causal}")
+        _run(w, wl.mask_spec(w), row_split=2)
+
+
+def test_row_split_hand_masks():
+    """Rows of 0, 1 and several tiles (one group then has no tile) and the
+    bigbird full size on sampled rows, split over two groups."""
+    require_gpu()
+    nb, block, d = 6, 64, 64
+    rows = [[], [0, 1, 3, 5], [2], [], [0, 4], [1, 2, 3, 4, 5]]
+    for causal in (True, False):
+        announce(f"[bsa] row split hand mask causal={causal}")
+        mask, rp, ci = _hand_mask(rows, nb, causal)
+        q, k, v = wl.make_qkv(1, 2, nb * block, d, torch.bfloat16, 93)
+        o, lse = api.sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask, 0.125, row_split=2)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, block, causal, 0.125)
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"split hand causal={causal}")
+    w = dict(wl.BLOCK_WORKLOADS["bigbird"], name="bigbird/split")
+    _run(w, workload_spec(w), samples=_samples(w["B"], w["H"], w["N"], w["block"], 64, 8), row_split=2)
