@@ -152,7 +152,8 @@ def test_out_of_range_columns_are_skipped():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_gqa_and_strided_inputs():
+@pytest.mark.parametrize("row_split", [1, 2])
+def test_gqa_and_strided_inputs(row_split):
     require_gpu()
     B, H, Hkv, N, d, block = 2, 4, 2, 1024, 64, 64
     spec = dict(num_blocks=N // block, num_groups=1, causal=True, win_before=2, win_after=0,
@@ -165,8 +166,8 @@ def test_gqa_and_strided_inputs():
     qs = q.transpose(1, 2).contiguous().cuda().transpose(1, 2)
     ks = k.transpose(1, 2).contiguous().cuda().transpose(1, 2)
     vs = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)
-    announce("[bsa] gqa + strided")
-    o, lse = api.sparse_attn_fwd(qs, ks, vs, mask)
+    announce(f"[bsa] gqa + strided row_split={row_split}")
+    o, lse = api.sparse_attn_fwd(qs, ks, vs, mask, row_split=row_split)
     torch.cuda.synchronize()
     rp, ci, _ = bm.build(spec)
     o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, block, True, 1 / math.sqrt(d))
@@ -183,9 +184,13 @@ def test_determinism_and_schedule_invariance():
     o1, l1 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0)
     o2, l2 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0)
     o3, l3 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, use_schedule=False)
+    # split rows: deterministic as well (a fixed merge order of the two groups)
+    o4, l4 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, row_split=2)
+    o5, l5 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, row_split=2, use_schedule=False)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    assert torch.equal(o4, o5) and torch.equal(l4, l5)
 
 
 def test_zero_query_counts_keys():
