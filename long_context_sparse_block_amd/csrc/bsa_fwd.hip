@@ -12,9 +12,10 @@
 //   * one workgroup per (batch, head, query block); one wave per 32 queries;
 //     optionally NP groups of waves split the row's key tiles and merge;
 //   * key blocks are walked in 64-key tiles copied global -> LDS by direct
-//     (DMA) loads into rings of K and V slots; for d = 64 the K ring runs one
-//     tile ahead so that S(n+1) is computed on the matrix cores while the
-//     softmax of tile n runs on the VALU;
+//     (DMA) loads into K and V slots: one slot each for whole rows (small LDS
+//     footprint, many resident workgroups), a ring for split rows at d = 64
+//     whose K side runs one tile ahead so that S(n+1) is computed on the
+//     matrix cores while the softmax of tile n runs on the VALU;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so every lane owns one query
 //     column: the row max / sum of the online softmax are in-lane except for a
 //     single exchange with lane ^ 32 (v_permlane32_swap);
@@ -108,14 +109,23 @@ __device__ __forceinline__ int64_t next_entry(const BsaArgs& a, const Item& it, 
 // tile of the row; the groups' partial softmax states are merged through LDS
 // at the end.
 //
-// Per group the tiles form a software pipeline: while the softmax of tile n
-// runs on the VALU, the MFMAs of S(n+1) = K(n+1) Q^T are already in flight, and
-// the MFMAs of O += V(n) P(n) overlap the bookkeeping of the next step.  K and
-// V travel global -> LDS by direct (DMA) loads into two rings of S slots; the K
-// ring runs one tile ahead of the V ring, so at step n the slots of K(n+1) and
-// V(n) are read while K(n+S) and V(n+S-1) are in flight.  The row's key-block
-// ids are held in VGPR lanes and read with v_readlane, so the loop issues no
-// memory access besides the DMA and LDS operand reads.
+// K and V travel global -> LDS by direct (DMA) loads into two rings of S
+// slots.  Two shapes of the tile loop:
+//   * one slot (S = 1, not pipelined; the row_split = 1 configurations): step n
+//     computes S(n), the softmax and O += V(n) P(n), then, after a barrier,
+//     copies tile n+1 into the slots.  The copy latency of a tile is covered by
+//     the other resident workgroups rather than by a deeper ring: with 16 KiB
+//     of LDS per workgroup (d = 64) occupancy is set by registers alone, four
+//     waves per SIMD at d = 64 (three at d = 128), which measured faster than
+//     two slots with fewer resident workgroups;
+//   * pipelined (PIPE, S >= 2; the d = 64 split-row configurations): while the
+//     softmax of tile n runs on the VALU, the MFMAs of S(n+1) = K(n+1) Q^T are
+//     already in flight, and the MFMAs of O += V(n) P(n) overlap the
+//     bookkeeping of the next step; the K ring runs one tile ahead of the V
+//     ring, so at step n the slots of K(n+1) and V(n) are read while K(n+S) and
+//     V(n+S-1) are in flight.
+// The row's key-block ids are held in VGPR lanes and read with v_readlane, so
+// the loop issues no memory access besides the DMA and LDS operand reads.
 
 // Workgroup barrier that does not drain outstanding DMA loads (a fenced
 // barrier would wait for every in-flight tile, not just the one needed).
@@ -163,18 +173,18 @@ struct BsaCfg {
   static constexpr int KVB = 64 * ROWB;        // bytes of one K (or V) tile
   static constexpr int SLOTB = NP * KVB;       // one ring slot: a tile per group
   static constexpr int VRING = S * SLOTB;      // offset of the V ring
-  static constexpr int LDSB = 2 * S * SLOTB;
+  static constexpr int RINGB = 2 * S * SLOTB;
   static constexpr int JN = KVB / 16 / (QW * 64);  // DMA loads per thread per tile
   // K operand k-steps of the next tile read at the top of a step (the rest
   // are read inside the MFMA / softmax interleave)
   static constexpr int KPRE = SA_KPRE < D / 16 ? SA_KPRE : D / 16;
   static constexpr int KPA = KPRE > 0 ? KPRE : 1;
-  static_assert(S >= 2 && S <= 3, "2 or 3 ring slots");
+  static_assert(S >= 1 && S <= 3 && (S >= 2 || !PIPE), "1 to 3 ring slots, at least 2 when pipelined");
   static_assert(JN >= 1 && (KVB / 16) % (QW * 64) == 0, "tiles must split evenly over a group");
   static_assert(4 * JN < 64, "vmcnt range");
   // merge area: per (group > 0, wave, lane): O^T partial (D/2 floats), m, l
   static constexpr int MERGEB = (NP - 1) * QW * 64 * (D / 2 + 2) * 4;
-  static_assert(MERGEB <= LDSB, "merge area must fit in the rings");
+  static constexpr int LDSB = RINGB > MERGEB ? RINGB : MERGEB;  // dynamic LDS bytes
 };
 
 template <int D, int BLK, int NP, int S, bool PIPE>
@@ -360,6 +370,11 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
           dma_k(n + S, qn, pn);
         }
         if (n + S - 1 < NI) dma_v(n + S - 1, S > 2 ? q2 : q1, (pn + S - 1) % S);
+      } else if constexpr (S == 1) {
+        // K(n) and V(n) must have landed (copied at the end of step n-1)
+        wait_vmcnt<0>();
+        ring_barrier();
+        qk(kring_p, cur);
       } else {
         // K(n) and V(n) must have landed; the barrier also frees tile n-1
         if (S == 3)
@@ -411,9 +426,9 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
         if (S > 2) {
           q0 = q1;
           q1 = qn;
-        } else {
+        } else if (S == 2) {
           q0 = qn;
-        }
+        }  // one slot: q0 moves on at the end of the step
       }
 
       // tile max over both half-rows, in log2 units (max3 chains)
@@ -499,6 +514,16 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
       }
       SA_SCHED_GROUP(0x002, 128);
       SA_SCHED_GROUP(0x008, 4 * (D / 32));
+      if constexpr (!PIPE && S == 1) {
+        if (n + 1 < NI) {
+          // every wave has read tile n (its LDS reads returned): refill the slots
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          ring_barrier();
+          q0 = tile_kb(n + 1);
+          dma_k(n + 1, q0, 0);
+          dma_v(n + 1, q0, 0);
+        }
+      }
     };
 
     using yes = std::true_type;
@@ -648,18 +673,20 @@ sa_status launch(Kern kern, const BsaArgs& a, int threads, int lds_bytes, hipStr
 }
 
 // (groups per workgroup NP, ring slots S, software-pipelined S(n+1)) of each
-// compiled tile shape
+// compiled tile shape.  One slot, not pipelined, for whole rows: 4 % (long rows)
+// to 12 % faster than a two-slot ring on the compression-guided, gzip-guided
+// and long-context masks, from the higher occupancy
 #ifndef SA_CFG_64_64
-#define SA_CFG_64_64 1, 2, true
+#define SA_CFG_64_64 1, 1, false
 #endif
 #ifndef SA_CFG_64_128
-#define SA_CFG_64_128 1, 2, true
+#define SA_CFG_64_128 1, 1, false
 #endif
 #ifndef SA_CFG_128_64
-#define SA_CFG_128_64 1, 2, false
+#define SA_CFG_128_64 1, 1, false
 #endif
 #ifndef SA_CFG_128_128
-#define SA_CFG_128_128 1, 2, false
+#define SA_CFG_128_128 1, 1, false
 #endif
 // ... and with each row split over two wave groups (row_split = 2)
 #ifndef SA_CFG2_64_64
