@@ -121,9 +121,8 @@ __device__ __forceinline__ void store_f(typename Elem<BF16>::T* p, const float* 
 __device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * sa::kLog2e; }
 
 // ---------------------------------------------------------------- delta ----
-// D[b, h, t] = <dO_t, o_t>; D/8 lanes per row, 8 elements each.  STAT: store
-// the pair {lse log2(e), D} of the row instead of D alone.
-template <int D, bool BF16, bool STAT>
+// D[b, h, t] = <dO_t, o_t>; D/8 lanes per row, 8 elements each.
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   typedef typename Elem<BF16>::T T;
   constexpr int LPR = D / 8;
@@ -143,12 +142,7 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
   for (int j = 0; j < 8; ++j) s = fmaf(x[j], y[j], s);
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
-  if (live && part == 0) {
-    if constexpr (STAT)
-      a.stat[rr] = sa::f32x2{lse2_of(a.lse[rr]), s};
-    else
-      a.delta[rr] = s;
-  }
+  if (live && part == 0) a.delta[rr] = s;
 }
 
 // ------------------------------------------------------- mask transpose ----
@@ -498,8 +492,22 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
     qb[u] = *(const sa::u32x4*)(Q + tq * a.st[TQ][2] + 16 * u + 8 * hl);
     gb[u] = *(const sa::u32x4*)(G + tq * a.st[TDO][2] + 16 * u + 8 * hl);
   }
-  const sa::f32x2 st2 = *(const sa::f32x2*)(a.stat + ((int64_t)b * a.H + h) * a.N + tq);
-  const float l2 = st2[0], dd = st2[1];
+  // the row statistics: D = <dO, o> (this lane holds d 16u + 8 hl .. + 7, the
+  // other half in lane ^ 32) and lse in log2 units; stored for the dK/dV kernel
+  const uint16_t* Ov = (const uint16_t*)a.o + b * a.st[TO][0] + h * a.st[TO][1];
+  float dsum = 0.f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const sa::u32x4 ob = *(const sa::u32x4*)(Ov + tq * a.st[TO][2] + 16 * u + 8 * hl);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      dsum = __builtin_fmaf(sa::bf16_lo(ob[x]), sa::bf16_lo(gb[u][x]), dsum);
+      dsum = __builtin_fmaf(sa::bf16_hi(ob[x]), sa::bf16_hi(gb[u][x]), dsum);
+    }
+  }
+  const int64_t srow = ((int64_t)b * a.H + h) * a.N + tq;
+  const float dd = sa::sum_xor32(dsum), l2 = lse2_of(a.lse[srow]);
+  if (hl == 0) a.stat[srow] = sa::f32x2{l2, dd};
   sa::f32x16 acc[NT];
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::f32x16{};
@@ -1129,18 +1137,14 @@ sa_status common_args(BwdArgs& a, int32_t dtype, const void* q, const void* k, c
   return SA_OK;
 }
 
-sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, bool stat, hipStream_t stream) {
+sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   const int64_t blocks = (rows * (d / 8) + 255) / 256;
-  if (dtype == SA_BF16) {
-    if (stat)
-      return d == 64 ? launch(delta_kernel<64, true, true>, a, blocks, 256, 0, stream, "delta_kernel")
-                     : launch(delta_kernel<128, true, true>, a, blocks, 256, 0, stream, "delta_kernel");
-    return d == 64 ? launch(delta_kernel<64, true, false>, a, blocks, 256, 0, stream, "delta_kernel")
-                   : launch(delta_kernel<128, true, false>, a, blocks, 256, 0, stream, "delta_kernel");
-  }
-  return d == 64 ? launch(delta_kernel<64, false, false>, a, blocks, 256, 0, stream, "delta_kernel")
-                 : launch(delta_kernel<128, false, false>, a, blocks, 256, 0, stream, "delta_kernel");
+  if (dtype == SA_BF16)
+    return d == 64 ? launch(delta_kernel<64, true>, a, blocks, 256, 0, stream, "delta_kernel")
+                   : launch(delta_kernel<128, true>, a, blocks, 256, 0, stream, "delta_kernel");
+  return d == 64 ? launch(delta_kernel<64, false>, a, blocks, 256, 0, stream, "delta_kernel")
+                 : launch(delta_kernel<128, false>, a, blocks, 256, 0, stream, "delta_kernel");
 }
 
 // 64-row tiles per dK/dV work item: longer columns are split over several
@@ -1266,8 +1270,10 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
   a.col_capacity = col_capacity, a.row_capacity = row_capacity;
   a.nb = N / block, a.G = num_groups, a.mbs = mask_batch_stride, a.mhs = mask_head_stride, a.causal = causal;
   const bool bf = dtype == SA_BF16;
-  st = launch_delta(a, dtype, d, bf, stream);
-  if (st != SA_OK) return st;
+  if (!bf) {  // the bf16 dQ kernel computes the row statistics itself
+    st = launch_delta(a, dtype, d, stream);
+    if (st != SA_OK) return st;
+  }
   if (d == 64) return block == 64 ? launch_bsa_bwd<64, 64>(a, bf, stream) : launch_bsa_bwd<64, 128>(a, bf, stream);
   return block == 64 ? launch_bsa_bwd<128, 64>(a, bf, stream) : launch_bsa_bwd<128, 128>(a, bf, stream);
 }
@@ -1288,7 +1294,7 @@ extern "C" sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k
   }
   a.noff = num_offsets;
   for (int n = 0; n < num_offsets; ++n) a.offs[n] = offsets[n];
-  st = launch_delta(a, dtype, d, false, stream);
+  st = launch_delta(a, dtype, d, stream);
   if (st != SA_OK) return st;
   const int64_t tiles = ((int64_t)N + 255) / 256;
   const int64_t nq = (int64_t)B * H * tiles, nk = (int64_t)B * H_kv * tiles;
