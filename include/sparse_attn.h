@@ -148,8 +148,10 @@ typedef struct sa_mask_desc {
                                    flags (explicit or drawn) as group g / P     */
 } sa_mask_desc;
 
-/* Upper bound on the number of CSR entries the mask can have:
- * G * N_b * (N_b + 1) / 2 when causal, G * N_b * N_b otherwise.
+/* Entries col_idx must hold for sparse_attn_build_mask: the largest number of
+ * CSR entries the mask can have (G * N_b * (N_b + 1) / 2 when causal,
+ * G * N_b * N_b otherwise) plus G * N_b entries of scratch (the row lengths,
+ * kept past the CSR while it is built).
  * Returns a negative sa_status if the description is invalid. */
 int64_t sparse_attn_mask_capacity(const sa_mask_desc* desc);
 
@@ -165,8 +167,10 @@ sa_status sparse_attn_check_mask_desc(const sa_mask_desc* desc);
  *   sched    DEVICE int32 [G][N_b] or NULL: per group, the row ids ordered by
  *            decreasing row length, ties by increasing row id (a longest-first
  *            launch order for sparse_attn_fwd).
- * Three kernels (count, prefix sum, fill) on `stream`; the result is unique
- * (bit-exact for a given description).
+ * Kernels on `stream`: count, then fill with the prefix sum folded in (up to
+ * 8192 rows; larger masks take a separate prefix-sum kernel between them).
+ * The result is unique (bit-exact for a given description); col_idx entries
+ * past the CSR are scratch.
  */
 sa_status sparse_attn_build_mask(const sa_mask_desc* desc, int32_t* row_ptr, int32_t* col_idx,
                                  int64_t col_capacity, int32_t* sched, hipStream_t stream);

@@ -1,4 +1,8 @@
 // Device construction of the block-mask CSR: count -> prefix sum -> fill.
+// Up to kDirectRows rows the prefix sum is folded into the fill: the counts go
+// to scratch entries of col_idx past the largest possible CSR, and every fill
+// workgroup sums the counts of the rows before its own (two launches instead
+// of three).
 //
 // Row (g, i) of the mask is the union, in block units, of the identity, the
 // local window, the global blocks, the random draws and the literal blocks
@@ -16,6 +20,7 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kScanThreads = 1024;
+constexpr int64_t kDirectRows = 8192;
 
 struct MaskArgs {
   int32_t nb, G, causal, wb, wa, clamp;
@@ -32,6 +37,7 @@ struct MaskArgs {
   int32_t* col_idx;
   int64_t col_capacity;
   int32_t* sched;
+  int32_t* counts;  // [G * nb] row lengths (direct mode), else nullptr
 };
 
 // Everything a wave needs to decide membership for one row.
@@ -148,8 +154,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void mask_count_kernel(MaskArg
     count += __popcll(__ballot(m));
   }
   if (lane == 0) {
-    a.row_ptr[r + 1] = count;
-    if (r == 0) a.row_ptr[0] = 0;
+    if (a.counts) {
+      a.counts[r] = count;
+    } else {
+      a.row_ptr[r + 1] = count;
+      if (r == 0) a.row_ptr[0] = 0;
+    }
   }
 }
 
@@ -179,11 +189,32 @@ __global__ __launch_bounds__(kScanThreads) void mask_scan_kernel(MaskArgs a) {
 
 __global__ __launch_bounds__(64 * kWavesPerBlock) void mask_fill_kernel(MaskArgs a) {
   __shared__ int32_t draws[kWavesPerBlock][SA_MAX_RANDOM + 1];
+  __shared__ int64_t wsum[kWavesPerBlock];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int64_t r0 = (int64_t)blockIdx.x * kWavesPerBlock, r = r0 + wave;
+  const int64_t R = (int64_t)a.G * a.nb;
+  int64_t start = 0;
+  if (a.counts) {
+    // entries before this block's first row: the sum of the earlier counts
+    int64_t s = 0;
+    for (int64_t x = threadIdx.x; x < r0; x += 64 * kWavesPerBlock) s += a.counts[x];
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) wsum[wave] = s;
+    __syncthreads();
+    for (int w = 0; w < kWavesPerBlock; ++w) start += wsum[w];
+    for (int w = 0; w < wave; ++w)
+      if (r0 + w < R) start += a.counts[r0 + w];
+  }
   const RowCtx c = setup_row(a, r, draws[wave], lane);
   if (!c.valid) return;
-  const int32_t start = a.row_ptr[r];
+  if (a.counts) {
+    if (lane == 0) {
+      a.row_ptr[r + 1] = (int32_t)(start + a.counts[r]);
+      if (r == 0) a.row_ptr[0] = 0;
+    }
+  } else {
+    start = a.row_ptr[r];
+  }
   int32_t run = 0;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int32_t j0 = 0; j0 < a.nb; j0 += 64) {
@@ -199,15 +230,23 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void mask_fill_kernel(MaskArgs
   if (a.sched) {
     // rank of this row in the group's longest-first order (ties: lower id first)
     const int32_t* rp = a.row_ptr + (int64_t)c.g * a.nb;
-    const int32_t mine = rp[c.i + 1] - rp[c.i];
+    const int32_t* cn = a.counts ? a.counts + (int64_t)c.g * a.nb : nullptr;
+    auto len = [&](int32_t x) { return cn ? cn[x] : rp[x + 1] - rp[x]; };
+    const int32_t mine = len(c.i);
     int32_t rank = 0;
     for (int32_t x = lane; x < a.nb; x += 64) {
-      const int32_t other = rp[x + 1] - rp[x];
+      const int32_t other = len(x);
       rank += (other > mine) || (other == mine && x < c.i);
     }
     for (int off = 32; off > 0; off >>= 1) rank += __shfl_xor(rank, off);
     if (lane == 0) a.sched[(int64_t)c.g * a.nb + rank] = c.i;
   }
+}
+
+// Largest possible number of CSR entries.
+int64_t entry_bound(const sa_mask_desc* d) {
+  const int64_t G = d->num_groups, nb = d->num_blocks;
+  return d->causal ? G * nb * (nb + 1) / 2 : G * nb * nb;
 }
 
 sa_status check_desc(const sa_mask_desc* d) {
@@ -235,9 +274,7 @@ sa_status check_desc(const sa_mask_desc* d) {
   if (d->literal_mode != SA_LIT_NONE && d->literal_flags == nullptr &&
       !(d->literal_p >= 0.0 && d->literal_p <= 1.0))
     return SA_ERR_INVALID;
-  const int64_t cap = d->causal ? (int64_t)d->num_groups * d->num_blocks * (d->num_blocks + 1) / 2
-                                : (int64_t)d->num_groups * d->num_blocks * d->num_blocks;
-  if (cap > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
+  if (entry_bound(d) + (int64_t)d->num_groups * d->num_blocks > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
 
@@ -250,8 +287,7 @@ sa_status sparse_attn_check_mask_desc(const sa_mask_desc* desc) { return check_d
 int64_t sparse_attn_mask_capacity(const sa_mask_desc* d) {
   const sa_status st = check_desc(d);
   if (st != SA_OK) return st;
-  const int64_t G = d->num_groups, nb = d->num_blocks;
-  return d->causal ? G * nb * (nb + 1) / 2 : G * nb * nb;
+  return entry_bound(d) + (int64_t)d->num_groups * d->num_blocks;  // + scratch for the row lengths
 }
 
 sa_status sparse_attn_build_mask(const sa_mask_desc* d, int32_t* row_ptr, int32_t* col_idx,
@@ -290,13 +326,16 @@ sa_status sparse_attn_build_mask(const sa_mask_desc* d, int32_t* row_ptr, int32_
   a.col_capacity = col_capacity;
   a.sched = sched;
   const int64_t R = (int64_t)a.G * a.nb;
+  a.counts = R <= kDirectRows ? col_idx + entry_bound(d) : nullptr;
   const unsigned grid = (unsigned)((R + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL(mask_count_kernel, dim3(grid), dim3(64 * kWavesPerBlock), 0, stream, a);
   sa_status e = sa_host::check_launch("mask_count_kernel");
   if (e != SA_OK) return e;
-  hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
-  e = sa_host::check_launch("mask_scan_kernel");
-  if (e != SA_OK) return e;
+  if (!a.counts) {
+    hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
+    e = sa_host::check_launch("mask_scan_kernel");
+    if (e != SA_OK) return e;
+  }
   hipLaunchKernelGGL(mask_fill_kernel, dim3(grid), dim3(64 * kWavesPerBlock), 0, stream, a);
   return sa_host::check_launch("mask_fill_kernel");
 }

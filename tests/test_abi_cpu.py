@@ -81,8 +81,9 @@ def test_mask_desc_errors(lib, over, status):
 
 
 def test_mask_capacity(lib):
-    assert api.sparse_attn_mask_capacity(_spec()) == 8 * 9 // 2
-    assert api.sparse_attn_mask_capacity(_spec(causal=False, num_groups=3)) == 3 * 64
+    # the largest possible CSR plus one scratch entry per row (row lengths)
+    assert api.sparse_attn_mask_capacity(_spec()) == 8 * 9 // 2 + 8
+    assert api.sparse_attn_mask_capacity(_spec(causal=False, num_groups=3)) == 3 * 64 + 3 * 8
     assert api.sparse_attn_check_mask_desc(_spec()) == L.SA_OK
 
 

@@ -53,6 +53,17 @@ def test_bigbird_union_size_and_components():
     assert nnz <= 636
 
 
+@pytest.mark.parametrize("G", [16, 17])
+def test_row_count_both_build_paths(G):
+    """8192 rows (prefix sum folded into the fill) and 8704 rows (separate
+    prefix-sum kernel): both bit-exact."""
+    require_gpu()
+    spec = dict(num_blocks=512, num_groups=G, causal=True, win_before=3, win_after=0, win_clamp=False,
+                global_blocks=[0], num_random=2, random_blocks=None, literal_mode="pair",
+                literal_flags=None, literal_p=0.2, seed=31)
+    _check_csr(spec, f"rows={G * 512}")
+
+
 def test_explicit_flags_and_draws_bitexact():
     require_gpu()
     G, nb, r = 3, 77, 4
