@@ -69,6 +69,7 @@ enum {
 #define SA_MAX_BLOCKS 16384 /* blocks per sequence (num_blocks)            */
 #define SA_MAX_OFFSETS 128 /* distances per offset table                   */
 #define SA_MAX_RUNGS 64    /* interpolated rungs per offset call            */
+#define SA_MAX_SPLIT_WAYS 16 /* workgroups sharing one split forward row    */
 
 /*
  * Block mask description (HOST struct, passed by host pointer).
@@ -225,6 +226,24 @@ sa_status sparse_attn_literal_flags(const uint8_t* bytes, int32_t G, int64_t n_b
  *              (global rows of a non-causal mask), more waves per row
  *              otherwise.  Same results up to fp32 summation order; the fp32
  *              path ignores it.
+ *   split_rows 0 .. N_b (else SA_ERR_INVALID), bf16 with row_split = 1 only
+ *              (SA_ERR_INVALID otherwise; the fp32 path ignores it): the rows
+ *              at the first split_rows launch positions of every (b, h) --
+ *              the longest ones when sched is the longest-first order -- are
+ *              each run by split_ways workgroups, part p taking the row's key
+ *              tiles p, p + split_ways, ...; the last part to finish merges
+ *              the partial softmax states.  Shortens the critical path of rows
+ *              much longer than the rest (the global rows of a non-causal
+ *              mask); results equal those of whole rows up to fp32 summation
+ *              order (bit-identical from launch to launch).
+ *   split_ways 2 .. SA_MAX_SPLIT_WAYS when split_rows > 0 (else ignored).
+ *   workspace  DEVICE, 16-byte aligned, when split_rows > 0 (else ignored,
+ *              may be NULL): workspace_bytes >= sparse_attn_fwd_workspace_bytes
+ *              (B, H, d, block, split_rows, split_ways) (SA_ERR_CAPACITY
+ *              otherwise; SA_ERR_NULL when NULL).  Its first B*H*split_rows
+ *              int32 are arrival counters that must be zero when the
+ *              workspace is first used; every launch leaves them zero.
+ *              Launches that share a workspace must not overlap in time.
  *   SA_ERR_UNSUPPORTED for bf16 when a K or V sequence stride is >= 2^24
  *              elements.
  */
@@ -233,7 +252,14 @@ sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const voi
                           int32_t block, const int64_t* strides, const int32_t* row_ptr,
                           const int32_t* col_idx, int64_t col_capacity, const int32_t* sched,
                           int32_t num_groups, int64_t mask_batch_stride, int64_t mask_head_stride,
-                          int32_t causal, float scale, int32_t row_split, hipStream_t stream);
+                          int32_t causal, float scale, int32_t row_split, int32_t split_rows,
+                          int32_t split_ways, void* workspace, int64_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Bytes of the split-row workspace of sparse_attn_fwd: 0 when split_rows = 0;
+ * SA_ERR_INVALID / SA_ERR_UNSUPPORTED (negative) for invalid sizes. */
+int64_t sparse_attn_fwd_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t block, int32_t split_rows,
+                                        int32_t split_ways);
 
 /*
  * Offset table of "Depth-Staggered Fibonacci Spacing for Sparse Attention",

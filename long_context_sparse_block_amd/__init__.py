@@ -20,7 +20,9 @@ from .api import (  # noqa: F401
     offset_attn_make_table,
     offset_attn_make_table_ratio,
     power2_base,
+    fwd_workspace,
     row_split_for,
+    split_rows_for,
     sparse_attn_bwd,
     sparse_attn_build_mask,
     sparse_attn_check_mask_desc,

@@ -36,6 +36,7 @@ SA_MAX_BLOCKS = 16384
 SA_MAX_OFFSETS = 128
 SA_MAX_PERIOD = 64
 SA_MAX_RUNGS = 64
+SA_MAX_SPLIT_WAYS = 16
 
 # every function the header declares, with (restype, argtypes)
 _i32, _i64, _f32, _f64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint64
@@ -70,7 +71,8 @@ SIGNATURES = {
     "sparse_attn_build_mask": (_i32, [ctypes.POINTER(MaskDesc), _p, _p, _i64, _p, _p]),
     "sparse_attn_fwd": (_i32, [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(_i64), _p, _p, _i64, _p, _i32, _i64, _i64, _i32,
-                               _f32, _i32, _p]),
+                               _f32, _i32, _i32, _i32, _p, _i64, _p]),
+    "sparse_attn_fwd_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sparse_attn_literal_flags": (_i32, [_p, _i32, _i64, _i32, _i32, _p, _p]),
     "offset_attn_make_table": (_i32, [_i32, _f64, ctypes.POINTER(_i64), _i32, _i32,
                                       ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),

@@ -208,16 +208,47 @@ def _strides(*ts):
 
 
 def row_split_for(spec):
-    """Wave groups per mask row for the bf16 forward: 2 when the spec has global
-    blocks and is not causal (its global rows then list every block, far more
-    than the other rows, and would otherwise bound the launch), else 1."""
-    return 2 if (not spec.get("causal", True)) and len(spec.get("global_blocks") or []) > 0 else 1
+    """Wave groups per mask row for the bf16 forward: 1.  Rows much longer than
+    the rest (the global rows of a non-causal mask) are split over several
+    workgroups instead (split_rows_for), which measured faster than splitting
+    every row over two wave groups (row_split = 2, still available)."""
+    return 1
+
+
+def split_rows_for(spec, row_split=1):
+    """(split_rows, split_ways) for the bf16 forward: the rows at the first
+    split_rows launch positions of every head (the longest ones) are each run
+    by split_ways workgroups.  Used for non-causal masks with global blocks,
+    whose global rows list every block while the other rows list about
+    window + globals + random ones: those rows are split into as many parts
+    (2 .. 16) as make a part about as long as an ordinary row.  (0, 2)
+    otherwise, and with row_split = 2."""
+    glob = len(spec.get("global_blocks") or [])
+    if row_split != 1 or spec.get("causal", True) or glob == 0:
+        return 0, 2
+    nb = int(spec["num_blocks"])
+    ordinary = int(spec.get("win_before") or 0) + int(spec.get("win_after") or 0) + 1 + glob + \
+        int(spec.get("num_random") or 0)
+    ways = max(2, min(L.SA_MAX_SPLIT_WAYS, -(-nb // max(1, ordinary))))
+    return min(glob, nb), ways
+
+
+def fwd_workspace(B, H, d, block, split_rows, split_ways, device):
+    """Zero-filled uint8 workspace for sparse_attn_fwd's split rows (None when
+    split_rows is 0); reusable by later launches of the same or smaller size."""
+    n = L.lib().sparse_attn_fwd_workspace_bytes(B, H, d, block, int(split_rows), int(split_ways))
+    if n < 0:
+        raise SparseAttnError(int(n), "sparse_attn_fwd_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
 
 
 def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_stride=0,
-                    use_schedule=True, out=None, lse=None, row_split=1):
+                    use_schedule=True, out=None, lse=None, row_split=1, split_rows=0, split_ways=2,
+                    workspace=None):
     """Block-sparse attention; returns (o, lse).  ``mask`` is a BlockMask;
-    ``row_split`` (1 or 2) as for the C entry point (see row_split_for)."""
+    ``row_split`` (1 or 2), ``split_rows`` and ``split_ways`` as for the C entry
+    point (see row_split_for, split_rows_for).  A zero-filled workspace is
+    allocated when split_rows > 0 and none is given."""
     B, H, Hkv, N, d = _check_qkv(q, k, v)
     if N % mask.num_blocks:
         raise ValueError("N must be a multiple of the number of mask blocks")
@@ -226,11 +257,14 @@ def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_st
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     sched = mask.sched if use_schedule else None
+    if split_rows > 0 and workspace is None and q.dtype == torch.bfloat16:
+        workspace = fwd_workspace(B, H, d, block, split_rows, split_ways, q.device)
     st = L.lib().sparse_attn_fwd(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, block,
         _strides(q, k, v, o), _ptr(mask.row_ptr), _ptr(mask.col_idx), mask.col_idx.numel(),
         _ptr(sched), mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal),
-        scale, int(row_split), _stream(q.device))
+        scale, int(row_split), int(split_rows), int(split_ways), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(q.device))
     _check(st, "sparse_attn_fwd")
     return o, lse_t
 
@@ -428,10 +462,14 @@ class BlockSparsePlan:
 
     ``build_mask()`` and ``forward()`` each make one C call and allocate
     nothing; outputs land in ``self.mask``, ``self.o`` and ``self.lse``.
-    ``row_split`` defaults to ``row_split_for(spec)``.
+    ``row_split`` defaults to ``row_split_for(spec)``, (``split_rows``,
+    ``split_ways``) to ``split_rows_for(spec, row_split)`` (no split rows
+    without a launch schedule or for fp32); the split-row workspace is
+    allocated once, zero-filled.
     """
 
-    def __init__(self, spec, q, k, v, scale=None, use_schedule=True, row_split=None):
+    def __init__(self, spec, q, k, v, scale=None, use_schedule=True, row_split=None, split_rows=None,
+                 split_ways=None):
         B, H, Hkv, N, d = _check_qkv(q, k, v)
         self.device = q.device
         self._keep = []
@@ -452,11 +490,17 @@ class BlockSparsePlan:
         self.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
         self.mbs = int(spec.get("mask_batch_stride", 0))
         self.mhs = int(spec.get("mask_head_stride", 0))
+        self.row_split = row_split_for(spec) if row_split is None else int(row_split)
+        auto_rows, auto_ways = split_rows_for(spec, self.row_split) if use_schedule else (0, 2)
+        self.split_rows = int(auto_rows if split_rows is None else split_rows) if q.dtype == torch.bfloat16 else 0
+        self.split_ways = int(auto_ways if split_ways is None else split_ways)
+        self.workspace = fwd_workspace(B, H, d, N // nb, self.split_rows, self.split_ways, q.device)
         self._fwd_args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(self.o), _ptr(self.lse), B, H,
                           Hkv, N, d, N // nb, _strides(q, k, v, self.o), _ptr(self.mask.row_ptr),
                           _ptr(self.mask.col_idx), self.mask.col_idx.numel(), _ptr(self.mask.sched),
                           G, self.mbs, self.mhs, int(self._desc.causal), self.scale,
-                          row_split_for(spec) if row_split is None else int(row_split))
+                          self.row_split, self.split_rows, self.split_ways, _ptr(self.workspace),
+                          self.workspace.numel() if self.workspace is not None else 0)
         self._mask_args = (ctypes.byref(self._desc), _ptr(self.mask.row_ptr), _ptr(self.mask.col_idx),
                            self.mask.col_idx.numel(), _ptr(self.mask.sched))
         self._lib = L.lib()

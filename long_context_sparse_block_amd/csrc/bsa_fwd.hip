@@ -56,6 +56,12 @@ struct BsaArgs {
   float scale;       // logit scale
   float scale_log2;  // |scale| * log2(e) (bf16 path), never 0
   uint32_t qsign;    // bf16 pair sign mask folded into Q when scale < 0
+  // Split rows (whole-row kernels only): the first split_rows launch positions
+  // of every head are each run by split_ways workgroups, part p taking tiles
+  // p, p + split_ways, ...; their partial softmax states meet in the workspace.
+  int32_t split_rows, split_ways;
+  int32_t* split_cnt;  // [B * H * split_rows] arrival counters, 0 between launches
+  float* split_part;   // [B * H * split_rows][split_ways] partial states
 };
 
 // Work item of a workgroup: head (b, h), query block i, CSR entry range.
@@ -188,7 +194,11 @@ struct BsaCfg {
 };
 
 template <int D, int BLK, int NP, int S, bool PIPE>
-__global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArgs a) {
+// Whole-row kernels keep the register count of 4 (d = 64) or 3 (d = 128) waves
+// per SIMD.
+__global__ __launch_bounds__(BLK / 32 * NP * 64)
+__attribute__((amdgpu_waves_per_eu(NP == 1 && !PIPE ? (D == 128 ? 3 : 4) : 1)))
+void bsa_fwd_bf16_kernel(BsaArgs a) {
   using C = BsaCfg<D, BLK, NP, S, PIPE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -197,8 +207,30 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
   const int grp = wave / C::QW, wq = wave % C::QW;
   const int hl = lane >> 5, lq = lane & 31;
 
-  const Item it = work_item(a);
+  // Work unit: a whole row, or one part of a split row (whole-row kernels):
+  // per head, units W p .. W p + W - 1 are the parts of the row at launch
+  // position p < split_rows (W = split_ways), unit u >= W split_rows the row at
+  // u - (W - 1) split_rows.
+  Item it;
+  int part = -1;  // >= 0: this workgroup takes tiles part, part + W, ... of the row
+  int32_t unit_bh = 0, unit_pos = 0;
+  if (NP == 1 && a.split_rows > 0) {
+    const int32_t BH = a.B * a.H, W = a.split_ways;
+    const int32_t u = blockIdx.x / BH;
+    unit_bh = blockIdx.x - u * BH;
+    if (u < W * a.split_rows) {
+      unit_pos = u / W;
+      part = u - unit_pos * W;
+    } else {
+      unit_pos = u - (W - 1) * a.split_rows;
+    }
+    it = work_item_at(a, unit_bh, unit_pos);
+  } else {
+    it = work_item(a);
+  }
   if (!it.ok) return;
+  const int np = part >= 0 ? a.split_ways : NP;  // tile stride of this group
+  const int gs = part >= 0 ? part : grp;         // ... and its first tile
 
   const uint16_t* Q = (const uint16_t*)a.q + it.b * a.qs[0] + it.h * a.qs[1];
   const uint16_t* K = (const uint16_t*)a.k + it.b * a.ks[0] + it.kvh * a.ks[1];
@@ -288,17 +320,17 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
     first_pass = false;
 
     const int T = cnt * C::SUBS;       // 64-key tiles of this pass
-    const int NI = (T + NP - 1) / NP;  // pipeline steps of each group
+    const int NI = (T + np - 1) / np;  // pipeline steps of each group
 
     // Key block of this group's tile at step m, or -1 when the tile is past
     // the end of the pass or its id is outside [0, limit) (such tiles are
     // loaded from a safe block and fully masked).
     auto tile_kb = [&](int m) -> int32_t {
-      const int t = m * NP + grp;
+      const int t = m * np + gs;
       const int32_t kb = sa::readlane(lst, min(t, T - 1) / C::SUBS);
       return (t < T && (uint32_t)kb < (uint32_t)limit) ? kb : -1;
     };
-    auto tile_sub = [&](int m) -> int { return C::SUBS == 1 ? 0 : min(m * NP + grp, T - 1) % C::SUBS; };
+    auto tile_sub = [&](int m) -> int { return C::SUBS == 1 ? 0 : min(m * np + gs, T - 1) % C::SUBS; };
     auto dma_k = [&](int m, int32_t kb, int slot) {
       dma_tile(K, kbs, ks2, offK, offK4, k_contig, kring, slot, kb < 0 ? it.i : kb, tile_sub(m));
     };
@@ -550,6 +582,60 @@ __global__ __launch_bounds__(BLK / 32 * NP * 64) void bsa_fwd_bf16_kernel(BsaArg
 
   // merge the groups' partial states into group 0
   l_run = sa::sum_xor32(l_run);
+
+  // Part of a split row: publish this part's state (O^T partial, m, l; per
+  // wave, element-major so each store covers 64 consecutive floats), then count
+  // the arrival.  The last of the W parts to arrive merges the W states, read
+  // back in part order so the result does not depend on the arrival order,
+  // finishes the row and sets the counter back to 0 for the next launch.  The
+  // states go through device-scope stores and loads (written through to, and
+  // read from, the device coherence point) rather than fences, which would
+  // write back and invalidate the whole L2 that the other workgroups of the XCD
+  // are reading K and V from.
+  if (NP == 1 && part >= 0) {
+    constexpr int PER = D / 2 + 2;
+    constexpr int64_t SLOTF = (int64_t)C::QW * PER * 64;  // floats per partial state
+    const int W = a.split_ways;
+    const int64_t row = (int64_t)unit_bh * a.split_rows + unit_pos;
+    float* const states = a.split_part + row * W * SLOTF + (int64_t)wq * PER * 64 + lane;
+    float* mine = states + part * SLOTF;
+    auto publish = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto fetch = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) publish(mine + (16 * dt + e) * 64, oacc[dt][e]);
+    publish(mine + (D / 2) * 64, m_used);
+    publish(mine + (D / 2 + 1) * 64, l_run);
+    wait_vmcnt<0>();  // this wave's stores have reached the coherence point
+    __syncthreads();  // ... and the other waves'; every wave is past its last tile
+    int* arrival = (int*)smem;
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(a.split_cnt + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == W - 1) __hip_atomic_store(a.split_cnt + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      arrival[0] = old;
+    }
+    __syncthreads();
+    if (arrival[0] != W - 1) return;
+    m_used = fetch(states + (D / 2) * 64);
+    l_run = fetch(states + (D / 2 + 1) * 64);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[dt][e] = fetch(states + (16 * dt + e) * 64);
+    for (int p = 1; p < W; ++p) {
+      const float* st = states + p * SLOTF;
+      const float mo = fetch(st + (D / 2) * 64), lo = fetch(st + (D / 2 + 1) * 64);
+      const float mm = fmaxf(m_used, mo);
+      const float a0 = sa::fast_exp2(m_used - mm), a1 = sa::fast_exp2(mo - mm);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] = oacc[dt][e] * a0 + fetch(st + (16 * dt + e) * 64) * a1;
+      l_run = l_run * a0 + lo * a1;
+      m_used = mm;
+    }
+  }
   if constexpr (NP > 1) {
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with the rings; reuse them
@@ -717,13 +803,35 @@ inline sa_status allow_lds(const void* kern, int bytes) {
     static const sa_status lds_ok =                                                          \
         allow_lds((const void*)&bsa_fwd_bf16_kernel<D, BLK, CFG>, Cf::LDSB);                  \
     if (lds_ok != SA_OK) return lds_ok;                                                      \
-    const int64_t grid = (int64_t)a.B * a.H * a.nb;                                          \
+    const int64_t grid = (int64_t)a.B * a.H * (a.nb + (int64_t)a.split_rows * (a.split_ways - 1)); \
     hipLaunchKernelGGL((bsa_fwd_bf16_kernel<D, BLK, CFG>), dim3((unsigned)grid), dim3(Cf::NT), \
                        Cf::LDSB, stream, a);                                                 \
     return sa_host::check_launch(NAME);                                                      \
   } while (0)
 
+// Split-row workspace: arrival counters, then two partial states per row.
+struct SplitLayout {
+  int64_t part, total;
+};
+inline SplitLayout split_layout(int64_t B, int64_t H, int64_t d, int64_t block, int64_t split_rows,
+                                int64_t split_ways) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  SplitLayout l;
+  l.part = up(B * H * split_rows * 4);
+  l.total = split_rows > 0 ? l.part + up(B * H * split_rows * split_ways * (block / 32) * 64 * (d / 2 + 2) * 4)
+                           : 0;
+  return l;
+}
+
 }  // namespace
+
+extern "C" int64_t sparse_attn_fwd_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t block,
+                                                   int32_t split_rows, int32_t split_ways) {
+  if (B < 1 || H < 1 || split_rows < 0) return SA_ERR_INVALID;
+  if (split_rows > 0 && (split_ways < 2 || split_ways > SA_MAX_SPLIT_WAYS)) return SA_ERR_INVALID;
+  if ((d != 64 && d != 128) || (block != 64 && block != 128)) return SA_ERR_UNSUPPORTED;
+  return split_layout(B, H, d, block, split_rows, split_ways).total;
+}
 
 extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                                      void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
@@ -731,9 +839,12 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
                                      const int32_t* row_ptr, const int32_t* col_idx,
                                      int64_t col_capacity, const int32_t* sched, int32_t num_groups,
                                      int64_t mask_batch_stride, int64_t mask_head_stride,
-                                     int32_t causal, float scale, int32_t row_split, hipStream_t stream) {
+                                     int32_t causal, float scale, int32_t row_split, int32_t split_rows,
+                                     int32_t split_ways, void* workspace, int64_t workspace_bytes,
+                                     hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !row_ptr || !col_idx) return SA_ERR_NULL;
   if (row_split != 1 && row_split != 2) return SA_ERR_INVALID;
+  if (split_rows < 0) return SA_ERR_INVALID;
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_INVALID;
   if (B < 1 || H < 1 || H_kv < 1 || N < 1 || d < 1 || block < 1) return SA_ERR_INVALID;
   if (H % H_kv != 0) return SA_ERR_INVALID;
@@ -746,7 +857,19 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   if (N % block != 0) return SA_ERR_INVALID;
   if ((d != 64 && d != 128) || (block != 64 && block != 128)) return SA_ERR_UNSUPPORTED;
   const int64_t nb = N / block;
-  if ((int64_t)B * H * nb > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
+  if (split_rows > nb) return SA_ERR_INVALID;
+  // split rows apply to the bf16 whole-row kernels; the fp32 path ignores them
+  const int32_t splits = dtype == SA_BF16 ? split_rows : 0;
+  if (splits > 0 && row_split != 1) return SA_ERR_INVALID;
+  if (splits > 0 && (split_ways < 2 || split_ways > SA_MAX_SPLIT_WAYS)) return SA_ERR_INVALID;
+  const int32_t ways = splits > 0 ? split_ways : 1;
+  if ((int64_t)B * H * (nb + (int64_t)splits * (ways - 1)) > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
+  const SplitLayout sl = split_layout(B, H, d, block, splits, ways);
+  if (splits > 0) {
+    if (!workspace) return SA_ERR_NULL;
+    if (!sa_host::aligned16(workspace)) return SA_ERR_INVALID;
+    if (workspace_bytes < sl.total) return SA_ERR_CAPACITY;
+  }
   if (!sa_host::aligned16(q) || !sa_host::aligned16(k) || !sa_host::aligned16(v) ||
       !sa_host::aligned16(o))
     return SA_ERR_INVALID;
@@ -770,6 +893,10 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   // then rounds to 0 exactly as before, while masked logits still scale to -inf.
   a.scale_log2 = scale != 0.f ? fabsf(scale) * sa::kLog2e : 1e-30f;
   a.qsign = scale < 0.f ? 0x80008000u : 0u;
+  a.split_rows = splits;
+  a.split_ways = ways;
+  a.split_cnt = splits > 0 ? (int32_t*)workspace : nullptr;
+  a.split_part = splits > 0 ? (float*)((uint8_t*)workspace + sl.part) : nullptr;
 
   if (dtype == SA_BF16 && row_split == 2) {
     if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG2_64_64, "bsa_fwd_bf16<64,64,split>");

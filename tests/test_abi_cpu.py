@@ -103,12 +103,24 @@ def _fwd(lib, **kw):
     fake = ctypes.c_void_p(1 << 20)
     a = dict(dtype=L.SA_BF16, q=fake, k=fake, v=fake, o=fake, lse=fake, B=1, H=2, H_kv=2, N=512,
              d=64, block=64, strides=None, row_ptr=fake, col_idx=fake, cap=100, sched=None, G=1,
-             mbs=0, mhs=0, causal=1, scale=0.125, row_split=1)
+             mbs=0, mhs=0, causal=1, scale=0.125, row_split=1, split_rows=0, split_ways=2, ws=None,
+             ws_bytes=0)
     a.update(kw)
     return lib.sparse_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
                                a["H_kv"], a["N"], a["d"], a["block"], a["strides"], a["row_ptr"],
                                a["col_idx"], a["cap"], a["sched"], a["G"], a["mbs"], a["mhs"],
-                               a["causal"], a["scale"], a["row_split"], None)
+                               a["causal"], a["scale"], a["row_split"], a["split_rows"], a["split_ways"],
+                               a["ws"], a["ws_bytes"], None)
+
+
+def _fwd_ws_bytes(B, H, d, block, split_rows, ways):
+    """Split-row workspace size: int32 counters, then one partial state per
+    part of each split row (per wave of 32 queries and lane: d/2 O^T values,
+    m, l as fp32), each region rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    if split_rows == 0:
+        return 0
+    return up(B * H * split_rows * 4) + up(B * H * split_rows * ways * (block // 32) * 64 * (d // 2 + 2) * 4)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -124,6 +136,15 @@ def _fwd(lib, **kw):
     (dict(scale=float("nan")), L.SA_ERR_INVALID),
     (dict(row_split=0), L.SA_ERR_INVALID),
     (dict(row_split=3), L.SA_ERR_INVALID),
+    (dict(split_rows=-1), L.SA_ERR_INVALID),
+    (dict(split_rows=9), L.SA_ERR_INVALID),          # more than N_b = 8 rows
+    (dict(split_rows=2, row_split=2), L.SA_ERR_INVALID),
+    (dict(split_rows=2), L.SA_ERR_NULL),             # no workspace
+    (dict(split_rows=2, ws=ctypes.c_void_p((1 << 20) + 8), ws_bytes=1 << 20), L.SA_ERR_INVALID),
+    (dict(split_rows=2, ws=ctypes.c_void_p(1 << 20), ws_bytes=_fwd_ws_bytes(1, 2, 64, 64, 2, 2) - 1),
+     L.SA_ERR_CAPACITY),
+    (dict(split_rows=2, split_ways=1, ws=ctypes.c_void_p(1 << 20), ws_bytes=1 << 20), L.SA_ERR_INVALID),
+    (dict(split_rows=2, split_ways=17, ws=ctypes.c_void_p(1 << 20), ws_bytes=1 << 20), L.SA_ERR_INVALID),
     (dict(cap=-1), L.SA_ERR_INVALID),
     (dict(q=ctypes.c_void_p((1 << 20) + 2)), L.SA_ERR_INVALID),  # misaligned
     (dict(strides=(ctypes.c_int64 * 12)(*([8192 * 64, 8192 * 64, 60] * 4))), L.SA_ERR_INVALID),
@@ -131,6 +152,23 @@ def _fwd(lib, **kw):
 ])
 def test_fwd_host_errors(lib, over, status):
     assert _fwd(lib, **over) == status
+
+
+@pytest.mark.parametrize("B,H,d,block,sr,ways", [(1, 2, 64, 64, 0, 2), (1, 2, 64, 64, 2, 2), (4, 8, 64, 64, 16, 3),
+                                                (2, 3, 128, 128, 5, 8), (1, 16, 128, 64, 64, 16),
+                                                (3, 1, 64, 128, 1, 2)])
+def test_fwd_workspace_bytes(lib, B, H, d, block, sr, ways):
+    assert lib.sparse_attn_fwd_workspace_bytes(B, H, d, block, sr, ways) == _fwd_ws_bytes(B, H, d, block, sr, ways)
+
+
+def test_fwd_workspace_bytes_errors(lib):
+    assert lib.sparse_attn_fwd_workspace_bytes(0, 1, 64, 64, 1, 2) == L.SA_ERR_INVALID
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 64, 64, -1, 2) == L.SA_ERR_INVALID
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 64, 64, 1, 1) == L.SA_ERR_INVALID
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 64, 64, 1, 17) == L.SA_ERR_INVALID
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 96, 64, 1, 2) == L.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 64, 32, 1, 2) == L.SA_ERR_UNSUPPORTED
+
 
 
 def _off(lib, offsets, **kw):
@@ -283,12 +321,26 @@ def test_bwd_workspace_bytes(lib):
 
 
 def test_plan_picks_row_split():
-    """Rows are split over two wave groups for non-causal masks with global
-    blocks only (their global rows list every block)."""
+    """Whole rows per workgroup everywhere (long rows are split across
+    workgroups instead, see test_plan_picks_split_rows)."""
     from long_context_sparse_block_amd import api
     from long_context_sparse_block_amd import workloads as wl
-    assert api.row_split_for(wl.mask_spec(wl.BLOCK_WORKLOADS["bigbird"])) == 2
-    for name in ("compression-guided", "long-context", "gzip-guided", "tiny-fp32"):
+    for name in ("bigbird", "compression-guided", "long-context", "gzip-guided", "tiny-fp32"):
         assert api.row_split_for(wl.mask_spec(wl.BLOCK_WORKLOADS[name])) == 1
-    assert api.row_split_for(api.mask_preset("longformer", 64, causal=False)) == 2
-    assert api.row_split_for(api.mask_preset("local-only", 64, causal=False)) == 1
+
+
+def test_plan_picks_split_rows():
+    """The global rows of non-causal masks with global blocks are split into
+    parts about as long as an ordinary row; nothing is split otherwise."""
+    from long_context_sparse_block_amd import api
+    from long_context_sparse_block_amd import workloads as wl
+    spec = lambda n: wl.mask_spec(wl.BLOCK_WORKLOADS[n])
+    assert api.split_rows_for(spec("bigbird")) == (2, 8)        # 64 blocks, 3 + 2 + 3 per ordinary row
+    assert api.split_rows_for(spec("bigbird"), row_split=2) == (0, 2)
+    for name in ("compression-guided", "long-context", "gzip-guided"):
+        assert api.split_rows_for(spec(name)) == (0, 2)
+    assert api.split_rows_for(api.mask_preset("local-only", 64, causal=False)) == (0, 2)
+    # 8 global blocks, +-4 window: ordinary rows 9 + 8 blocks -> ceil(64 / 17) = 4 parts
+    assert api.split_rows_for(api.mask_preset("longformer", 64, causal=False)) == (8, 4)
+    # 64 global blocks: ordinary rows 9 + 64 -> ceil(512 / 73) = 8 parts
+    assert api.split_rows_for(api.mask_preset("longformer", 512, causal=False)) == (64, 8)

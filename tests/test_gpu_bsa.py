@@ -18,7 +18,8 @@ from tests.gpu_util import announce, compare, f64, require_gpu, workload_spec
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, spec, B=None, H=None, samples=None, use_schedule=True, seed=None, row_split=1):
+def _run(w, spec, B=None, H=None, samples=None, use_schedule=True, seed=None, row_split=1, split_rows=0,
+         split_ways=2):
     """Run the GPU path for workload dict w (optionally fewer batch / heads) and
     compare against the oracle (all rows, or the given samples)."""
     B = w["B"] if B is None else B
@@ -30,7 +31,7 @@ def _run(w, spec, B=None, H=None, samples=None, use_schedule=True, seed=None, ro
     scale = 1.0 / math.sqrt(w["d"])
     mbs, mhs = spec["mask_batch_stride"], spec["mask_head_stride"]
     o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, scale, mbs, mhs, use_schedule=use_schedule,
-                                 row_split=row_split)
+                                 row_split=row_split, split_rows=split_rows, split_ways=split_ways)
     torch.cuda.synchronize()
     rp, ci, _ = bm.build(spec)
     q64, k64, v64 = f64(q), f64(k), f64(v)
@@ -152,8 +153,10 @@ def test_out_of_range_columns_are_skipped():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("row_split", [1, 2])
-def test_gqa_and_strided_inputs(row_split):
+@pytest.mark.parametrize("row_split,split_rows", [(1, 0), (2, 0), (1, 3)])
+def test_gqa_and_strided_inputs(row_split, split_rows):
+    """Grouped K/V heads and [B, N, H, d] storage, with and without split rows
+    (three parts each)."""
     require_gpu()
     B, H, Hkv, N, d, block = 2, 4, 2, 1024, 64, 64
     spec = dict(num_blocks=N // block, num_groups=1, causal=True, win_before=2, win_after=0,
@@ -166,8 +169,8 @@ def test_gqa_and_strided_inputs(row_split):
     qs = q.transpose(1, 2).contiguous().cuda().transpose(1, 2)
     ks = k.transpose(1, 2).contiguous().cuda().transpose(1, 2)
     vs = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)
-    announce(f"[bsa] gqa + strided row_split={row_split}")
-    o, lse = api.sparse_attn_fwd(qs, ks, vs, mask, row_split=row_split)
+    announce(f"[bsa] gqa + strided row_split={row_split} split_rows={split_rows}")
+    o, lse = api.sparse_attn_fwd(qs, ks, vs, mask, row_split=row_split, split_rows=split_rows, split_ways=3)
     torch.cuda.synchronize()
     rp, ci, _ = bm.build(spec)
     o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, block, True, 1 / math.sqrt(d))
@@ -187,10 +190,16 @@ def test_determinism_and_schedule_invariance():
     # split rows: deterministic as well (a fixed merge order of the two groups)
     o4, l4 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, row_split=2)
     o5, l5 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, row_split=2, use_schedule=False)
+    # rows split over two workgroups: the same from launch to launch (the two
+    # halves merge in a fixed order whichever finishes last)
+    ws = api.fwd_workspace(w["B"], w["H"], w["d"], w["block"], 32, 3, q.device)
+    o6, l6 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, split_rows=32, split_ways=3, workspace=ws)
+    o7, l7 = api.sparse_attn_fwd(q, k, v, mask, None, 1, 0, split_rows=32, split_ways=3, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
     assert torch.equal(o4, o5) and torch.equal(l4, l5)
+    assert torch.equal(o6, o7) and torch.equal(l6, l7)
 
 
 def test_zero_query_counts_keys():
@@ -272,3 +281,121 @@ def test_row_split_hand_masks():
         compare(o, lse, o_ref, l_ref, torch.bfloat16, f"split hand causal={causal}")
     w = dict(wl.BLOCK_WORKLOADS["bigbird"], name="bigbird/split")
     _run(w, workload_spec(w), samples=_samples(w["B"], w["H"], w["N"], w["block"], 64, 8), row_split=2)
+
+
+# ---- rows split over several workgroups (split_rows, split_ways) ----
+
+def test_split_rows_bigbird_reduced_full_parity():
+    """The plan's split of BigBird's global rows (two rows per head, eight
+    parts each), every output against the oracle."""
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS["bigbird"], name="bigbird/split-rows")
+    spec = workload_spec(dict(w, B=2, H=3))
+    sr, ways = api.split_rows_for(spec)
+    assert (sr, ways) == (2, 8)
+    announce(f"[bsa] split rows bigbird B=2 H=3 split_rows={sr} ways={ways}")
+    _run(w, spec, B=2, H=3, split_rows=sr, split_ways=ways)
+
+
+@pytest.mark.parametrize("name,B,H,ways", [("compression-guided", 4, 2, 2), ("gzip-guided", 4, 2, 3),
+                                           ("gzip-head-groups", 2, 12, 4)])
+def test_split_rows_causal_reduced_full_parity(name, B, H, ways):
+    """Causal masks with their longest eighth of the rows split."""
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS[name], name=name + "/split-rows")
+    spec = workload_spec(dict(w, B=B, H=H))
+    sr = (spec["num_blocks"] + 7) // 8
+    announce(f"[bsa] split rows {name} B={B} H={H} split_rows={sr} ways={ways}")
+    _run(w, spec, B=B, H=H, split_rows=sr, split_ways=ways)
+
+
+def test_split_rows_long_context_reduced_length():
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS["long-context"], N=8192, H=2, name="long-context-8k/split-rows")
+    announce("[bsa] split rows long-context N=8192 H=2 split_rows=8 ways=5")
+    _run(w, wl.mask_spec(w), split_rows=8, split_ways=5)
+
+
+@pytest.mark.parametrize("d,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_split_rows_tile_shapes(d, block):
+    """One split row and every row split, in 2 and 5 parts, causal and not, at
+    every tile shape."""
+    require_gpu()
+    N = 1024
+    for causal in (True, False):
+        for sr, ways in ((1, 2), (N // block, 5)):
+            w = dict(B=2, H=2, N=N, d=d, block=block, dtype="bf16", causal=causal, win_before=1,
+                     win_after=0 if causal else 1, win_clamp=False, global_blocks=[0], num_random=2,
+                     literal_mode="pair", literal_p=0.3, mask_seed=14, groups="per-sequence", qkv_seed=80,
+                     name=f"split-rows d{d}b{block} causal={causal} sr={sr} ways={ways}")
+            announce(f"[bsa] split rows d={d} block={block} causal={causal} split_rows={sr} ways={ways}")
+            _run(w, wl.mask_spec(w), split_rows=sr, split_ways=ways)
+
+
+def test_split_rows_hand_masks():
+    """Split rows without a launch order (positions are row ids), with rows of
+    0, 1 and several tiles: parts may have no tile, or only fully masked ones."""
+    require_gpu()
+    nb, block, d = 6, 64, 64
+    rows = [[], [0, 1, 3, 5], [2], [], [0, 4], [1, 2, 3, 4, 5]]
+    for causal in (True, False):
+        for sr, ways in ((1, 2), (3, 4), (nb, 2), (nb, 16)):
+            announce(f"[bsa] split rows hand mask causal={causal} split_rows={sr} ways={ways}")
+            mask, rp, ci = _hand_mask(rows, nb, causal)
+            q, k, v = wl.make_qkv(1, 2, nb * block, d, torch.bfloat16, 94)
+            o, lse = api.sparse_attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask, 0.125, split_rows=sr, split_ways=ways)
+            torch.cuda.synchronize()
+            o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, block, causal, 0.125)
+            compare(o, lse, o_ref, l_ref, torch.bfloat16, f"split-rows hand causal={causal} sr={sr} ways={ways}")
+
+
+def test_split_rows_workspace_reuse_and_counters():
+    """One workspace over several launches: bit-identical results, every
+    counter back at 0 after each launch, and later launches with other split
+    shapes on the same workspace still match the oracle."""
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS["bigbird"], name="split-rows reuse")
+    B, H = 2, 2
+    spec = wl.mask_spec(dict(w, B=B))
+    mask = api.sparse_attn_build_mask(spec)
+    q, k, v = wl.make_qkv(B, H, w["N"], w["d"], torch.bfloat16, 95)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ws = api.fwd_workspace(B, H, w["d"], w["block"], 16, 8, qd.device)
+    mbs, mhs = spec["mask_batch_stride"], spec["mask_head_stride"]
+    announce("[bsa] split rows workspace reuse")
+    outs = [api.sparse_attn_fwd(qd, kd, vd, mask, None, mbs, mhs, split_rows=2, split_ways=8, workspace=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    assert torch.all(ws[: B * H * 16 * 4] == 0)
+    rp, ci, _ = bm.build(spec)
+    o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, w["block"], False, 1 / math.sqrt(w["d"]),
+                                    mbs, mhs)
+    compare(outs[0][0], outs[0][1], o_ref, l_ref, torch.bfloat16, "split-rows reuse 2x8")
+    for sr, ways in ((16, 3), (5, 8)):
+        o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, None, mbs, mhs, split_rows=sr, split_ways=ways, workspace=ws)
+        torch.cuda.synchronize()
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"split-rows reuse {sr}x{ways}")
+        assert torch.all(ws[: B * H * 16 * 4] == 0)
+
+
+@pytest.mark.parametrize("name", ["bigbird", "compression-guided", "long-context"])
+def test_split_rows_full_size_sampled(name):
+    """Full workload sizes with split rows (the plan's split for BigBird, the
+    longest eighth in two parts otherwise), on sampled rows with the longest
+    rows -- the split ones -- included."""
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS[name], name=name + "/split-rows")
+    spec = workload_spec(w)
+    sr, ways = api.split_rows_for(spec)
+    if sr == 0:
+        sr, ways = (spec["num_blocks"] + 7) // 8, 2
+    rp, _, sched = bm.build(spec)
+    nb = spec["num_blocks"]
+    lens = np.diff(np.asarray(rp[: nb + 1]))
+    longest = int(np.argmax(lens))
+    samples = set(_samples(w["B"], w["H"], w["N"], w["block"], 64, 9))
+    samples |= {(0, 0, longest * w["block"]), (0, 0, longest * w["block"] + w["block"] - 1)}
+    announce(f"[bsa] split rows {name} full size sampled split_rows={sr} ways={ways}")
+    _run(w, spec, samples=sorted(samples), split_rows=sr, split_ways=ways)
