@@ -344,3 +344,18 @@ def test_plan_picks_split_rows():
     assert api.split_rows_for(api.mask_preset("longformer", 64, causal=False)) == (8, 4)
     # 64 global blocks: ordinary rows 9 + 64 -> ceil(512 / 73) = 8 parts
     assert api.split_rows_for(api.mask_preset("longformer", 512, causal=False)) == (64, 8)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus above 1 prints one JSON line that says
+    so and exits with status 2 before touching a device."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=300)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
