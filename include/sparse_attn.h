@@ -70,6 +70,7 @@ enum {
 #define SA_MAX_OFFSETS 128 /* distances per offset table                   */
 #define SA_MAX_RUNGS 64    /* interpolated rungs per offset call            */
 #define SA_MAX_SPLIT_WAYS 16 /* workgroups sharing one split forward row    */
+#define SA_SPLIT_COUNTERS 16384 /* split forward rows per launch (B * H * split_rows) */
 
 /*
  * Block mask description (HOST struct, passed by host pointer).
@@ -240,10 +241,14 @@ sa_status sparse_attn_literal_flags(const uint8_t* bytes, int32_t G, int64_t n_b
  *   workspace  DEVICE, 16-byte aligned, when split_rows > 0 (else ignored,
  *              may be NULL): workspace_bytes >= sparse_attn_fwd_workspace_bytes
  *              (B, H, d, block, split_rows, split_ways) (SA_ERR_CAPACITY
- *              otherwise; SA_ERR_NULL when NULL).  Its first B*H*split_rows
- *              int32 are arrival counters that must be zero when the
- *              workspace is first used; every launch leaves them zero.
- *              Launches that share a workspace must not overlap in time.
+ *              otherwise; SA_ERR_NULL when NULL).  Its first
+ *              SA_SPLIT_COUNTERS int32 (64 KiB, the same for every split
+ *              shape) are arrival counters that must be zero when the
+ *              workspace is first used; every launch leaves them zero, so a
+ *              workspace zeroed once serves later launches of any shape
+ *              whose size it covers.  Launches that share a workspace must
+ *              not overlap in time.
+ *              SA_ERR_UNSUPPORTED when B * H * split_rows > SA_SPLIT_COUNTERS.
  *   SA_ERR_UNSUPPORTED for bf16 when a K or V sequence stride is >= 2^24
  *              elements.
  */
@@ -256,8 +261,10 @@ sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const voi
                           int32_t split_ways, void* workspace, int64_t workspace_bytes,
                           hipStream_t stream);
 
-/* Bytes of the split-row workspace of sparse_attn_fwd: 0 when split_rows = 0;
- * SA_ERR_INVALID / SA_ERR_UNSUPPORTED (negative) for invalid sizes. */
+/* Bytes of the split-row workspace of sparse_attn_fwd: 0 when split_rows = 0,
+ * else 4 * SA_SPLIT_COUNTERS bytes of counters followed by the partial
+ * states; SA_ERR_INVALID / SA_ERR_UNSUPPORTED (negative) for invalid sizes
+ * (SA_ERR_UNSUPPORTED when B * H * split_rows > SA_SPLIT_COUNTERS). */
 int64_t sparse_attn_fwd_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t block, int32_t split_rows,
                                         int32_t split_ways);
 
@@ -403,6 +410,40 @@ sa_status offset_attn_bwd(int32_t dtype, const void* q, const void* k, const voi
                           const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta,
                           int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d, const int64_t* strides,
                           const int32_t* offsets, int32_t num_offsets, float scale, hipStream_t stream);
+
+/*
+ * The library's counter-based draws, evaluated on the host by the same code
+ * the mask kernels run (for checks without a GPU; no page fixes a generator,
+ * this is the library's convention).  sm = SplitMix64 output function (Steele,
+ * Lea & Flood, OOPSLA 2014).
+ *   sa_rng_key            key(seed, tag, a, b, c) = sm(sm(sm(sm(sm(seed) ^ tag) ^ a) ^ b) ^ c)
+ *   sa_rng_literal        the drawn literal flag of block `block` of flag group
+ *                         `group`: (key(seed, 1, group, block, 0) >> 32) <
+ *                         floor(p * 2^32) (clamped to [0, 2^32]) -> 1 / 0
+ *   sa_rng_random_blocks  the drawn random blocks of row `row` of group
+ *                         `group` over [0, n): candidate k = ((key(seed, 2,
+ *                         group, row, k) >> 32) * n) >> 32, repeats skipped,
+ *                         stop at min(r, n) values or 64 r candidates; writes
+ *                         them in draw order to `out` (HOST int32 [r]) and
+ *                         returns their count, or SA_ERR_NULL / SA_ERR_INVALID
+ *                         (n < 0, r < 0 or r > SA_MAX_RANDOM)
+ * sparse_attn_build_mask (literal_flags / random_blocks NULL) uses exactly these
+ * draws, with n = i (causal) or N_b (non-causal).
+ */
+uint64_t sa_rng_key(uint64_t seed, uint64_t tag, uint64_t a, uint64_t b, uint64_t c);
+int32_t sa_rng_literal(uint64_t seed, uint64_t group, uint64_t block, double p);
+int32_t sa_rng_random_blocks(uint64_t seed, uint64_t group, uint64_t row, int32_t n, int32_t r, int32_t* out);
+
+/*
+ * Shader-clock probe (measurement aid, not part of the attention path): one
+ * wave on `stream` counts shader-clock cycles (s_memtime) while at least
+ * `ticks` ticks of the constant-rate counter (s_memrealtime, the device's wall
+ * clock, 100 MHz on MI355X) pass, and writes out[0] = cycles, out[1] = ticks
+ * (DEVICE int64 [2]).  Run beside a workload on another stream, cycles / ticks
+ * x the wall-clock rate is the clock the workload ran at.
+ * 0 <= ticks <= 6e9 (else SA_ERR_INVALID).
+ */
+sa_status sa_clock_probe(int64_t* out, int64_t ticks, hipStream_t stream);
 
 const char* sa_status_string(sa_status s);
 const char* sa_last_hip_error(void);

@@ -37,6 +37,7 @@ SA_MAX_OFFSETS = 128
 SA_MAX_PERIOD = 64
 SA_MAX_RUNGS = 64
 SA_MAX_SPLIT_WAYS = 16
+SA_SPLIT_COUNTERS = 16384
 
 # every function the header declares, with (restype, argtypes)
 _i32, _i64, _f32, _f64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint64
@@ -93,6 +94,10 @@ SIGNATURES = {
                                _p]),
     "offset_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, _f32, _p]),
+    "sa_rng_key": (_u64, [_u64, _u64, _u64, _u64, _u64]),
+    "sa_rng_literal": (_i32, [_u64, _u64, _u64, _f64]),
+    "sa_rng_random_blocks": (_i32, [_u64, _u64, _u64, _i32, _i32, ctypes.POINTER(_i32)]),
+    "sa_clock_probe": (_i32, [_p, _i64, _p]),
     "sa_status_string": (ctypes.c_char_p, [_i32]),
     "sa_last_hip_error": (ctypes.c_char_p, []),
     "sa_version": (_i32, []),

@@ -235,7 +235,9 @@ def split_rows_for(spec, row_split=1):
 
 def fwd_workspace(B, H, d, block, split_rows, split_ways, device):
     """Zero-filled uint8 workspace for sparse_attn_fwd's split rows (None when
-    split_rows is 0); reusable by later launches of the same or smaller size."""
+    split_rows is 0).  Its counter area has a fixed size and every launch
+    leaves it zero, so it can be reused by later launches of any split shape
+    whose sparse_attn_fwd_workspace_bytes it covers (one launch at a time)."""
     n = L.lib().sparse_attn_fwd_workspace_bytes(B, H, d, block, int(split_rows), int(split_ways))
     if n < 0:
         raise SparseAttnError(int(n), "sparse_attn_fwd_workspace_bytes")
@@ -454,6 +456,23 @@ def offset_attn_fwd(q, k, v, offsets, scale=None, out=None, lse=None):
                                  _stream(q.device))
     _check(st, "offset_attn_fwd")
     return o, lse_t
+
+
+def capture_graph(fn):
+    """Record the launches fn() makes on the current device into a HIP graph
+    (torch.cuda.CUDAGraph; replay() re-issues them).  fn runs once eagerly on a
+    side stream first, so one-time set-up happens outside the capture.  The
+    library's launches contain no memset or allocation, so a plan's calls can
+    be captured as they are."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
 
 
 class BlockSparsePlan:

@@ -60,7 +60,7 @@ struct BsaArgs {
   // of every head are each run by split_ways workgroups, part p taking tiles
   // p, p + split_ways, ...; their partial softmax states meet in the workspace.
   int32_t split_rows, split_ways;
-  int32_t* split_cnt;  // [B * H * split_rows] arrival counters, 0 between launches
+  int32_t* split_cnt;  // arrival counter of split row bh * split_rows + pos, 0 between launches
   float* split_part;   // [B * H * split_rows][split_ways] partial states
 };
 
@@ -809,7 +809,10 @@ inline sa_status allow_lds(const void* kern, int bytes) {
     return sa_host::check_launch(NAME);                                                      \
   } while (0)
 
-// Split-row workspace: arrival counters, then two partial states per row.
+// Split-row workspace: a counter area of fixed size (SA_SPLIT_COUNTERS int32,
+// whatever the split shape, so that launches of any shape that share a
+// workspace find their counters at zero), then the partial states of every
+// part of every split row.
 struct SplitLayout {
   int64_t part, total;
 };
@@ -817,31 +820,20 @@ inline SplitLayout split_layout(int64_t B, int64_t H, int64_t d, int64_t block, 
                                 int64_t split_ways) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   SplitLayout l;
-  l.part = up(B * H * split_rows * 4);
+  l.part = (int64_t)SA_SPLIT_COUNTERS * 4;
   l.total = split_rows > 0 ? l.part + up(B * H * split_rows * split_ways * (block / 32) * 64 * (d / 2 + 2) * 4)
                            : 0;
   return l;
 }
 
-}  // namespace
-
-extern "C" int64_t sparse_attn_fwd_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t block,
-                                                   int32_t split_rows, int32_t split_ways) {
-  if (B < 1 || H < 1 || split_rows < 0) return SA_ERR_INVALID;
-  if (split_rows > 0 && (split_ways < 2 || split_ways > SA_MAX_SPLIT_WAYS)) return SA_ERR_INVALID;
-  if ((d != 64 && d != 128) || (block != 64 && block != 128)) return SA_ERR_UNSUPPORTED;
-  return split_layout(B, H, d, block, split_rows, split_ways).total;
-}
-
-extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
-                                     void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
-                                     int32_t N, int32_t d, int32_t block, const int64_t* strides,
-                                     const int32_t* row_ptr, const int32_t* col_idx,
-                                     int64_t col_capacity, const int32_t* sched, int32_t num_groups,
-                                     int64_t mask_batch_stride, int64_t mask_head_stride,
-                                     int32_t causal, float scale, int32_t row_split, int32_t split_rows,
-                                     int32_t split_ways, void* workspace, int64_t workspace_bytes,
-                                     hipStream_t stream) {
+// Checks every argument of sparse_attn_fwd and fills the kernel arguments;
+// nothing is launched.  The workspace pointer is only checked and stored.
+sa_status fwd_setup(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse, int32_t B,
+                    int32_t H, int32_t H_kv, int32_t N, int32_t d, int32_t block, const int64_t* strides,
+                    const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity, const int32_t* sched,
+                    int32_t num_groups, int64_t mask_batch_stride, int64_t mask_head_stride, int32_t causal,
+                    float scale, int32_t row_split, int32_t split_rows, int32_t split_ways, void* workspace,
+                    int64_t workspace_bytes, BsaArgs& a) {
   if (!q || !k || !v || !o || !lse || !row_ptr || !col_idx) return SA_ERR_NULL;
   if (row_split != 1 && row_split != 2) return SA_ERR_INVALID;
   if (split_rows < 0) return SA_ERR_INVALID;
@@ -863,6 +855,7 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   if (splits > 0 && row_split != 1) return SA_ERR_INVALID;
   if (splits > 0 && (split_ways < 2 || split_ways > SA_MAX_SPLIT_WAYS)) return SA_ERR_INVALID;
   const int32_t ways = splits > 0 ? split_ways : 1;
+  if ((int64_t)B * H * splits > SA_SPLIT_COUNTERS) return SA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * (nb + (int64_t)splits * (ways - 1)) > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
   const SplitLayout sl = split_layout(B, H, d, block, splits, ways);
   if (splits > 0) {
@@ -880,7 +873,7 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   if (dtype == SA_BF16 && (st[1].s >= (int64_t)1 << 24 || st[2].s >= (int64_t)1 << 24))
     return SA_ERR_UNSUPPORTED;
 
-  BsaArgs a = {};
+  a = BsaArgs{};
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
   int64_t* dst[4] = {a.qs, a.ks, a.vs, a.os};
   for (int t = 0; t < 4; ++t) dst[t][0] = st[t].b, dst[t][1] = st[t].h, dst[t][2] = st[t].s;
@@ -897,7 +890,12 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   a.split_ways = ways;
   a.split_cnt = splits > 0 ? (int32_t*)workspace : nullptr;
   a.split_part = splits > 0 ? (float*)((uint8_t*)workspace + sl.part) : nullptr;
+  return SA_OK;
+}
 
+// Launch of the kernel that serves (dtype, d, block, row_split).
+sa_status fwd_launch(const BsaArgs& a, int32_t dtype, int32_t d, int32_t block, int32_t row_split,
+                     hipStream_t stream) {
   if (dtype == SA_BF16 && row_split == 2) {
     if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG2_64_64, "bsa_fwd_bf16<64,64,split>");
     if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG2_64_128, "bsa_fwd_bf16<64,128,split>");
@@ -914,4 +912,32 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
   if (d == 64 && block == 128) return launch(bsa_fwd_f32_kernel<64, 128>, a, 128, 0, stream, "bsa_fwd_f32<64,128>");
   if (d == 128 && block == 64) return launch(bsa_fwd_f32_kernel<128, 64>, a, 64, 0, stream, "bsa_fwd_f32<128,64>");
   return launch(bsa_fwd_f32_kernel<128, 128>, a, 128, 0, stream, "bsa_fwd_f32<128,128>");
+}
+
+}  // namespace
+
+extern "C" int64_t sparse_attn_fwd_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t block,
+                                                   int32_t split_rows, int32_t split_ways) {
+  if (B < 1 || H < 1 || split_rows < 0) return SA_ERR_INVALID;
+  if (split_rows > 0 && (split_ways < 2 || split_ways > SA_MAX_SPLIT_WAYS)) return SA_ERR_INVALID;
+  if ((d != 64 && d != 128) || (block != 64 && block != 128)) return SA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * split_rows > SA_SPLIT_COUNTERS) return SA_ERR_UNSUPPORTED;
+  return split_layout(B, H, d, block, split_rows, split_ways).total;
+}
+
+extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                                     void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
+                                     int32_t N, int32_t d, int32_t block, const int64_t* strides,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t col_capacity, const int32_t* sched, int32_t num_groups,
+                                     int64_t mask_batch_stride, int64_t mask_head_stride,
+                                     int32_t causal, float scale, int32_t row_split, int32_t split_rows,
+                                     int32_t split_ways, void* workspace, int64_t workspace_bytes,
+                                     hipStream_t stream) {
+  BsaArgs a;
+  const sa_status st = fwd_setup(dtype, q, k, v, o, lse, B, H, H_kv, N, d, block, strides, row_ptr, col_idx,
+                                 col_capacity, sched, num_groups, mask_batch_stride, mask_head_stride, causal,
+                                 scale, row_split, split_rows, split_ways, workspace, workspace_bytes, a);
+  if (st != SA_OK) return st;
+  return fwd_launch(a, dtype, d, block, row_split, stream);
 }

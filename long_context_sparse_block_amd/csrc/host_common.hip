@@ -62,6 +62,39 @@ const char* sa_last_hip_error(void) { return g_last_error; }
 
 int32_t sa_version(void) { return 1; }
 
+}  // extern "C"
+
+namespace {
+
+// One lane reads the shader-clock counter (s_memtime) and the constant-rate
+// counter (s_memrealtime) at the start and once at least `ticks` constant-rate
+// ticks have passed (or after a bounded number of polls), and stores both
+// differences.
+__global__ __launch_bounds__(64) void clock_probe_kernel(int64_t* out, int64_t ticks) {
+  if (threadIdx.x != 0) return;
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  uint64_t r = r0;
+  for (int64_t n = 0; (int64_t)(r - r0) < ticks && n < (int64_t)1 << 32; ++n) {
+    __builtin_amdgcn_s_sleep(2);
+    r = __builtin_amdgcn_s_memrealtime();
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  out[0] = (int64_t)(c1 - c0);
+  out[1] = (int64_t)(r - r0);
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_clock_probe(int64_t* out, int64_t ticks, hipStream_t stream) {
+  if (out == nullptr) return SA_ERR_NULL;
+  if (ticks < 0 || ticks > (int64_t)100000000 * 60) return SA_ERR_INVALID;
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, stream, out, ticks);
+  return sa_host::check_launch("clock_probe_kernel");
+}
+
 int32_t sa_mask_desc_layout(int64_t* out, int32_t n) {
   const int64_t v[18] = {(int64_t)sizeof(sa_mask_desc),
                          (int64_t)offsetof(sa_mask_desc, num_blocks),

@@ -48,14 +48,13 @@ struct RowCtx {
   bool valid;
   bool row_global;
   bool lit_i;
-  uint64_t lit_key;  // key(seed, 1, g) prefix of the literal draws
+  uint64_t lit_key;  // key_prefix(seed, 1, flag group) of the literal draws
   int32_t ndraw;     // accepted random blocks, stored in LDS
 };
 
 __device__ __forceinline__ bool literal_of(const MaskArgs& a, const RowCtx& c, int32_t j) {
   if (a.lit_flags) return a.lit_flags[(int64_t)c.fg * a.nb + j] != 0;
-  const uint64_t h = sa::splitmix64(sa::splitmix64(c.lit_key ^ (uint64_t)j) ^ 0ull);
-  return (h >> 32) < a.lit_thr;
+  return sa::literal_draw(c.lit_key, (uint64_t)j, a.lit_thr);
 }
 
 __device__ __forceinline__ bool is_global(const MaskArgs& a, int32_t j) {
@@ -75,7 +74,7 @@ __device__ RowCtx setup_row(const MaskArgs& a, int64_t r, int32_t* draws, int la
   c.fg = a.period > 0 ? c.g / a.period : c.g;
   c.excl = a.excl | (a.period > 0 ? a.period_excl[c.g % a.period] : 0);
   c.row_global = is_global(a, c.i);
-  c.lit_key = sa::splitmix64(sa::splitmix64(sa::splitmix64(a.seed) ^ 1ull) ^ (uint64_t)c.fg);
+  c.lit_key = sa::key_prefix(a.seed, sa::kTagLiteral, (uint64_t)c.fg);
   c.lit_i = (a.lit_mode != SA_LIT_NONE) && c.valid && literal_of(a, c, c.i);
   c.ndraw = 0;
   if (lane == 0 && c.valid && a.num_random > 0) {
@@ -92,15 +91,7 @@ __device__ RowCtx setup_row(const MaskArgs& a, int64_t r, int32_t* draws, int la
         if (!seen) draws[cnt++] = x;
       }
     } else if (want > 0) {
-      uint64_t rk = sa::splitmix64(a.seed) ^ 2ull;
-      rk = sa::splitmix64(sa::splitmix64(sa::splitmix64(rk) ^ (uint64_t)c.g) ^ (uint64_t)c.i);
-      for (int k = 0; k < 64 * a.num_random && cnt < want; ++k) {
-        const uint64_t h = sa::splitmix64(rk ^ (uint64_t)k);
-        const int32_t x = (int32_t)(((h >> 32) * (uint64_t)n) >> 32);
-        bool seen = false;
-        for (int m = 0; m < cnt; ++m) seen |= (draws[m] == x);
-        if (!seen) draws[cnt++] = x;
-      }
+      cnt = sa::draw_distinct(a.seed, (uint64_t)c.g, (uint64_t)c.i, n, a.num_random, draws);
     }
     draws[SA_MAX_RANDOM] = cnt;
   }
@@ -243,6 +234,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void mask_fill_kernel(MaskArgs
   }
 }
 
+// floor(p * 2^32) in double, clamped to [0, 2^32] (0 for p <= 0 or NaN).
+uint64_t literal_threshold(double p) {
+  const double t = floor(p * 4294967296.0);
+  return (p > 0.0) ? (uint64_t)fmin(t, 4294967296.0) : 0ull;
+}
+
 // Largest possible number of CSR entries.
 int64_t entry_bound(const sa_mask_desc* d) {
   const int64_t G = d->num_groups, nb = d->num_blocks;
@@ -315,11 +312,7 @@ sa_status sparse_attn_build_mask(const sa_mask_desc* d, int32_t* row_ptr, int32_
   a.excl = d->exclude_parts;
   a.period = d->group_period;
   for (int n = 0; n < d->group_period; ++n) a.period_excl[n] = d->period_exclude[n];
-  {
-    // floor(p * 2^32) in double, clamped to [0, 2^32]
-    const double t = floor(d->literal_p * 4294967296.0);
-    a.lit_thr = (d->literal_p > 0.0) ? (uint64_t)fmin(t, 4294967296.0) : 0ull;
-  }
+  a.lit_thr = literal_threshold(d->literal_p);
   a.seed = d->seed;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
@@ -338,6 +331,20 @@ sa_status sparse_attn_build_mask(const sa_mask_desc* d, int32_t* row_ptr, int32_
   }
   hipLaunchKernelGGL(mask_fill_kernel, dim3(grid), dim3(64 * kWavesPerBlock), 0, stream, a);
   return sa_host::check_launch("mask_fill_kernel");
+}
+
+uint64_t sa_rng_key(uint64_t seed, uint64_t tag, uint64_t a, uint64_t b, uint64_t c) {
+  return sa::key_finish(sa::key_prefix(seed, tag, a), b, c);
+}
+
+int32_t sa_rng_literal(uint64_t seed, uint64_t group, uint64_t block, double p) {
+  return sa::literal_draw(sa::key_prefix(seed, sa::kTagLiteral, group), block, literal_threshold(p)) ? 1 : 0;
+}
+
+int32_t sa_rng_random_blocks(uint64_t seed, uint64_t group, uint64_t row, int32_t n, int32_t r, int32_t* out) {
+  if (out == nullptr) return SA_ERR_NULL;
+  if (n < 0 || r < 0 || r > SA_MAX_RANDOM) return SA_ERR_INVALID;
+  return sa::draw_distinct(seed, group, row, n, r, out);
 }
 
 }  // extern "C"

@@ -55,12 +55,52 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014): advance by the
-// golden-ratio increment, then the 64-bit finaliser.
-__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+// golden-ratio increment, then the 64-bit finaliser.  Host and device: the
+// library's host RNG entry points run this same code, so it can be checked
+// without a GPU.
+__host__ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
   uint64_t z = x + 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
   return z ^ (z >> 31);
+}
+
+// Keys of the library's counter-based draws (its own convention: no page
+// fixes a generator): key(seed, tag, a, b, c) = sm(sm(sm(sm(sm(seed) ^ tag) ^
+// a) ^ b) ^ c), evaluated as a per-(seed, tag, a) prefix and a finishing step.
+__host__ __device__ __forceinline__ uint64_t key_prefix(uint64_t seed, uint64_t tag, uint64_t a) {
+  return splitmix64(splitmix64(splitmix64(seed) ^ tag) ^ a);
+}
+__host__ __device__ __forceinline__ uint64_t key_finish(uint64_t prefix, uint64_t b, uint64_t c) {
+  return splitmix64(splitmix64(prefix ^ b) ^ c);
+}
+constexpr uint64_t kTagLiteral = 1, kTagRandom = 2;
+
+// Literal flag of block j from its key prefix key_prefix(seed, 1, flag group):
+// the high 32 bits of key(seed, 1, f, j, 0) below floor(p * 2^32).
+__host__ __device__ __forceinline__ bool literal_draw(uint64_t prefix, uint64_t j, uint64_t threshold) {
+  return (key_finish(prefix, j, 0) >> 32) < threshold;
+}
+
+// The min(r, n) distinct uniform draws from [0, n) of row i of group g ("BigBird"
+// Sec. 2, G_R: r sampled key blocks per query block; distinct, as the Sec. 3
+// sketch takes a permutation prefix): candidate k is ((h >> 32) n) >> 32 with
+// h = key(seed, 2, g, i, k); repeats are skipped; at most 64 r candidates.
+// Writes the accepted values in draw order to out[0 .. count) and returns count.
+__host__ __device__ inline int32_t draw_distinct(uint64_t seed, uint64_t g, uint64_t i, int32_t n, int32_t r,
+                                                 int32_t* out) {
+  const int32_t want = r < n ? r : n;
+  int32_t cnt = 0;
+  if (want <= 0) return 0;
+  const uint64_t prefix = key_prefix(seed, kTagRandom, g);
+  for (int32_t k = 0; k < 64 * r && cnt < want; ++k) {
+    const uint64_t h = key_finish(prefix, i, (uint64_t)k);
+    const int32_t x = (int32_t)(((h >> 32) * (uint64_t)n) >> 32);
+    bool seen = false;
+    for (int32_t m = 0; m < cnt; ++m) seen |= (out[m] == x);
+    if (!seen) out[cnt++] = x;
+  }
+  return cnt;
 }
 
 __device__ __forceinline__ int wave_lane() { return __lane_id(); }

@@ -114,13 +114,14 @@ def _fwd(lib, **kw):
 
 
 def _fwd_ws_bytes(B, H, d, block, split_rows, ways):
-    """Split-row workspace size: int32 counters, then one partial state per
-    part of each split row (per wave of 32 queries and lane: d/2 O^T values,
-    m, l as fp32), each region rounded up to 256 bytes."""
+    """Split-row workspace size: a fixed area of SA_SPLIT_COUNTERS int32
+    counters (the same for every split shape), then one partial state per part
+    of each split row (per wave of 32 queries and lane: d/2 O^T values, m, l as
+    fp32), rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
     if split_rows == 0:
         return 0
-    return up(B * H * split_rows * 4) + up(B * H * split_rows * ways * (block // 32) * 64 * (d // 2 + 2) * 4)
+    return 4 * L.SA_SPLIT_COUNTERS + up(B * H * split_rows * ways * (block // 32) * 64 * (d // 2 + 2) * 4)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -168,6 +169,10 @@ def test_fwd_workspace_bytes_errors(lib):
     assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 64, 64, 1, 17) == L.SA_ERR_INVALID
     assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 96, 64, 1, 2) == L.SA_ERR_UNSUPPORTED
     assert lib.sparse_attn_fwd_workspace_bytes(1, 1, 64, 32, 1, 2) == L.SA_ERR_UNSUPPORTED
+    # more split rows than the fixed counter area holds
+    assert lib.sparse_attn_fwd_workspace_bytes(4, 8, 64, 64, L.SA_SPLIT_COUNTERS // 32, 2) > 0
+    assert lib.sparse_attn_fwd_workspace_bytes(4, 8, 64, 64, L.SA_SPLIT_COUNTERS // 32 + 1, 2) == \
+        L.SA_ERR_UNSUPPORTED
 
 
 
@@ -359,3 +364,43 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_library_rng_known_answer_vectors(lib):
+    """The library's draws, run on the host by the same inline code the mask
+    kernels run (sa_rng_*), reproduce the frozen vectors written from the
+    oracle."""
+    from tests.test_oracle_masks import read_rng_vectors
+    keys, lits, draws = read_rng_vectors()
+    for (s, t, a, b, c), want in keys:
+        assert lib.sa_rng_key(s, t, a, b, c) == want
+    for (s, g, j, p), want in lits:
+        assert lib.sa_rng_literal(s, g, j, p) == want
+    for (s, g, i, n, r), want in draws:
+        out = (ctypes.c_int32 * max(1, r))()
+        cnt = lib.sa_rng_random_blocks(s, g, i, n, r, out)
+        assert cnt == len(want) and list(out[:cnt]) == want
+
+
+def test_library_rng_matches_oracle_on_workloads(lib):
+    """Every drawn literal flag of the compression-guided and long-context
+    masks and every random draw of the BigBird mask, library host path vs
+    oracle; argument errors of the draw entry point."""
+    from long_context_sparse_block_amd import workloads as wl
+    from oracle import rng
+    for name in ("compression-guided", "long-context"):
+        w = wl.BLOCK_WORKLOADS[name]
+        G = w["B"] if w["groups"] == "per-sequence" else 1
+        nb = w["N"] // w["block"]
+        for g in range(G):
+            got = [lib.sa_rng_literal(w["mask_seed"], g, j, w["literal_p"]) for j in range(nb)]
+            assert got == [rng.literal_flag(w["mask_seed"], g, j, w["literal_p"]) for j in range(nb)], name
+    w = wl.BLOCK_WORKLOADS["bigbird"]
+    nb, r = w["N"] // w["block"], w["num_random"]
+    out = (ctypes.c_int32 * r)()
+    for i in range(nb):
+        cnt = lib.sa_rng_random_blocks(w["mask_seed"], 0, i, nb, r, out)
+        assert list(out[:cnt]) == rng.random_blocks(w["mask_seed"], 0, i, nb, r)
+    assert lib.sa_rng_random_blocks(1, 0, 0, 4, 2, None) == L.SA_ERR_NULL
+    assert lib.sa_rng_random_blocks(1, 0, 0, -1, 2, out) == L.SA_ERR_INVALID
+    assert lib.sa_rng_random_blocks(1, 0, 0, 4, L.SA_MAX_RANDOM + 1, out) == L.SA_ERR_INVALID

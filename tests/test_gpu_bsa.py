@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+from long_context_sparse_block_amd import _lib as L
 from long_context_sparse_block_amd import api
 from long_context_sparse_block_amd import workloads as wl
 from oracle import attention as oa
@@ -380,6 +381,34 @@ def test_split_rows_workspace_reuse_and_counters():
         assert torch.all(ws[: B * H * 16 * 4] == 0)
 
 
+def test_split_rows_workspace_reuse_other_counter_layout():
+    """A workspace sized and zeroed for (split_rows 2, 16 ways) reused by a
+    launch with more split rows and fewer ways (16 x 2: more counters, as many
+    partial states, the same byte count): the counter area has a fixed size,
+    so the second launch's counters are not the first launch's partial states,
+    and every launch matches the oracle."""
+    require_gpu()
+    w = dict(wl.BLOCK_WORKLOADS["bigbird"], name="split-rows reuse other layout")
+    B, H = 2, 3
+    spec = wl.mask_spec(dict(w, B=B))
+    mask = api.sparse_attn_build_mask(spec)
+    q, k, v = wl.make_qkv(B, H, w["N"], w["d"], torch.bfloat16, 96)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ws = api.fwd_workspace(B, H, w["d"], w["block"], 2, 16, qd.device)
+    need = L.lib().sparse_attn_fwd_workspace_bytes(B, H, w["d"], w["block"], 16, 2)
+    assert 0 < need <= ws.numel()
+    mbs, mhs = spec["mask_batch_stride"], spec["mask_head_stride"]
+    rp, ci, _ = bm.build(spec)
+    o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, w["block"], False, 1 / math.sqrt(w["d"]),
+                                    mbs, mhs)
+    for sr, ways in ((2, 16), (16, 2), (2, 16), (16, 2)):
+        announce(f"[bsa] split rows workspace {sr}x{ways} after other layouts")
+        o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, None, mbs, mhs, split_rows=sr, split_ways=ways, workspace=ws)
+        torch.cuda.synchronize()
+        compare(o, lse, o_ref, l_ref, torch.bfloat16, f"split-rows reuse {sr}x{ways}")
+        assert torch.all(ws[: 4 * L.SA_SPLIT_COUNTERS] == 0)
+
+
 @pytest.mark.parametrize("name", ["bigbird", "compression-guided", "long-context"])
 def test_split_rows_full_size_sampled(name):
     """Full workload sizes with split rows (the plan's split for BigBird, the
@@ -399,3 +428,36 @@ def test_split_rows_full_size_sampled(name):
     samples |= {(0, 0, longest * w["block"]), (0, 0, longest * w["block"] + w["block"] - 1)}
     announce(f"[bsa] split rows {name} full size sampled split_rows={sr} ways={ways}")
     _run(w, spec, samples=sorted(samples), split_rows=sr, split_ways=ways)
+
+
+def test_bigbird_step_as_captured_graph():
+    """The BigBird step (mask build + forward with split rows) captured into a
+    HIP graph and replayed several times, with eager work of the library and of
+    torch between the replays: every replay equals the eager result bit for
+    bit, and the eager result matches the oracle."""
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS["bigbird"]
+    B, H = 1, 4
+    spec = wl.mask_spec(dict(w, B=B))
+    q, k, v = wl.make_qkv(B, H, w["N"], w["d"], torch.bfloat16, 97)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    announce("[bsa] bigbird step as a captured graph")
+    plan = api.BlockSparsePlan(spec, qd, kd, vd)
+    assert plan.split_rows > 0
+    plan()
+    torch.cuda.synchronize()
+    o_eager, l_eager = plan.o.clone(), plan.lse.clone()
+    rp, ci, _ = bm.build(spec)
+    o_ref, l_ref = oa.csr_attention(f64(q), f64(k), f64(v), rp, ci, w["block"], False, 1 / math.sqrt(w["d"]))
+    compare(o_eager, l_eager, o_ref, l_ref, torch.bfloat16, "bigbird eager")
+    g = api.capture_graph(plan)
+    other = api.BlockSparsePlan(spec, kd, qd, vd)  # eager work in between, other inputs
+    for rep in range(4):
+        plan.o.zero_()
+        plan.lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.o, o_eager) and torch.equal(plan.lse, l_eager), f"replay {rep}"
+        other()
+        _ = (qd.float() * 2).sum()
+        torch.cuda.synchronize()

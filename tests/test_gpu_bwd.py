@@ -168,14 +168,17 @@ def test_bsa_bwd_bf16_full_size_sampled_heads():
     _check_all(got, ref, torch.bfloat16, "full", heads=heads)
 
 
-def _off_case(offs, B, H, Hkv, N, d, dtype, seed, scale):
+def _off_case(offs, B, H, Hkv, N, d, dtype, seed, scale, offs_ref=None):
+    """Offset backward on the GPU over ``offs`` and the oracle's gradients over
+    ``offs_ref`` (the oracle's own table; default ``offs``)."""
+    offs_ref = offs if offs_ref is None else offs_ref
     q, k, v = wl.make_qkv(B, H, N, d, dtype, seed, H_kv=Hkv)
     do = _dout(q.shape, dtype, seed + 1)
     qd, kd, vd, dod = [t.cuda() for t in (q, k, v, do)]
     o, lse = api.offset_attn_fwd(qd, kd, vd, offs, scale)
     got = api.offset_attn_bwd(qd, kd, vd, o, lse, dod, offs, scale)
     torch.cuda.synchronize()
-    ref = ob.offset_attention_bwd(f64(q), f64(k), f64(v), f64(do), offs, scale, mags=True)
+    ref = ob.offset_attention_bwd(f64(q), f64(k), f64(v), f64(do), offs_ref, scale, mags=True)
     return got, ref
 
 
@@ -184,9 +187,10 @@ def _off_case(offs, B, H, Hkv, N, d, dtype, seed, scale):
 def test_offset_bwd_ragged_gqa(dtype, d):
     require_gpu()
     for N, Hkv in ((1, 2), (63, 1), (300, 2), (1000, 1)):
-        offs = oo.offset_table(5, 1.3, oo.fibonacci_base(N), N)
+        offs = api.offset_attn_make_table(5, 1.3, api.fibonacci_base(N), N)
+        offs_ref = oo.offset_table(5, 1.3, oo.fibonacci_base(N), N)
         announce(f"[bwd] offsets N={N} d={d} {dtype} H_kv={Hkv}")
-        got, ref = _off_case(offs, 2, 2, Hkv, N, d, dtype, 600 + N, 0.2)
+        got, ref = _off_case(offs, 2, 2, Hkv, N, d, dtype, 600 + N, 0.2, offs_ref)
         _check_all(got, ref, dtype, f"offsets N={N}")
 
 
@@ -201,10 +205,11 @@ def test_offset_bwd_workload_reduced_batch():
     require_gpu()
     ow = wl.OFFSET_WORKLOAD
     for N in ow["lengths"]:
-        offs = oo.offset_table(ow["W"], ow["alphas"][7], oo.fibonacci_base(N), N)
+        offs = api.offset_attn_make_table(ow["W"], ow["alphas"][7], api.fibonacci_base(N), N)
+        offs_ref = oo.offset_table(ow["W"], ow["alphas"][7], oo.fibonacci_base(N), N)
         announce(f"[bwd] offsets workload N={N} B=1 H=2")
         got, ref = _off_case(offs, 1, 2, 2, N, ow["d"], torch.bfloat16, ow["qkv_seed_base"][N] + 7,
-                             1 / math.sqrt(ow["d"]))
+                             1 / math.sqrt(ow["d"]), offs_ref)
         _check_all(got, ref, torch.bfloat16, f"offsets workload N={N}")
 
 
@@ -264,3 +269,79 @@ def test_bsa_bwd_bf16_split_columns_block64(H, Hkv):
     announce(f"[bwd] split columns H={H} Hkv={Hkv}")
     got, ref = _bsa_case(spec, 1, H, Hkv, nb * block, d, torch.bfloat16, 97)
     _check_all(got, ref, torch.bfloat16, f"split columns H={H} Hkv={Hkv}")
+
+
+def _long_rows(nb, causal, lo, seed, every=1):
+    """Hand CSR rows: every ``every``-th row lists between ``lo`` and all of its
+    allowed key blocks (more than one 64-entry pass of the dQ walk), the other
+    rows 1 to 4; entries ascending and unique, at random positions."""
+    R = np.random.default_rng(seed)
+    rows = []
+    for i in range(nb):
+        n_allowed = i + 1 if causal else nb
+        want = int(R.integers(lo, nb + 1)) if i % every == 0 else int(R.integers(1, 5))
+        k = min(n_allowed, want)
+        rows.append(sorted(int(c) for c in R.choice(n_allowed, size=k, replace=False)))
+    return rows
+
+
+@pytest.mark.parametrize("dtype,d,block,nb,H,Hkv", [
+    (torch.bfloat16, 64, 64, 140, 2, 1),
+    (torch.bfloat16, 128, 64, 140, 1, 1),
+    (torch.bfloat16, 64, 128, 80, 2, 1),
+    (torch.bfloat16, 128, 128, 80, 1, 1),
+    (torch.float32, 64, 64, 140, 1, 1),
+    (torch.float32, 128, 128, 80, 1, 1),
+])
+def test_bsa_bwd_rows_longer_than_one_pass(dtype, d, block, nb, H, Hkv):
+    """Rows of 65 to nb key blocks: the dQ walk takes a row's list in passes of
+    64 entries (two passes above 64, three above 128 at 140 blocks), and the
+    transposed columns, listed by up to nb query blocks of each q head, are
+    split into several dK / dV work items.  Causal and non-causal, element by
+    element against the oracle's gradients."""
+    require_gpu()
+    N = nb * block
+    for causal in (False, True):
+        rows = _long_rows(nb, causal, 65, 500 + nb + d + block, every=1 if block == 64 else 4)
+        longest = max(len(r) for r in rows)
+        assert longest > 64
+        announce(f"[bwd] long rows {dtype} d={d} block={block} nb={nb} H={H}/{Hkv} causal={causal} "
+                 f"longest={longest}")
+        q, k, v = wl.make_qkv(1, H, N, d, dtype, 900 + d + block, H_kv=Hkv)
+        do = _dout(q.shape, dtype, 901 + d + block)
+        qd, kd, vd, dod = [t.cuda() for t in (q, k, v, do)]
+        mask, rp, ci = _hand_mask(rows, nb, causal)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = api.sparse_attn_fwd(qd, kd, vd, mask, scale)
+        got = api.sparse_attn_bwd(qd, kd, vd, o, lse, dod, mask, None, scale)
+        torch.cuda.synchronize()
+        ref = ob.csr_attention_bwd(f64(q), f64(k), f64(v), f64(do), rp, ci, block, causal, scale, mags=True)
+        _check_all(got, ref, dtype, f"long rows d={d} b={block} causal={causal}")
+
+
+def test_bsa_bwd_long_context_full_size_sampled_heads():
+    """The long-context workload at full size ([1, 16, 65536, 128], block 128),
+    run as the bench runs it; whole heads 0 and 15 checked against the oracle.
+    19 of its 512 rows list 65 to 83 key blocks (a second dQ pass) and the four
+    global key blocks are listed by every later query block (16 dK / dV work
+    items each)."""
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS["long-context"]
+    spec = workload_spec(w)
+    rp, ci, _ = bm.build(spec)
+    assert int(np.diff(rp).max()) > 64
+    sel = [0, w["H"] - 1]
+    announce(f"[bwd] long-context full size {w['B']}x{w['H']}x{w['N']}x{w['d']}, heads {sel}")
+    q, k, v = wl.make_qkv(w["B"], w["H"], w["N"], w["d"], torch.bfloat16, w["qkv_seed"])
+    do = _dout(q.shape, torch.bfloat16, w["qkv_seed"] + 1)
+    plan = api.BlockSparsePlan(spec, q.cuda(), k.cuda(), v.cuda())
+    plan()
+    bp = api.BlockSparseBwdPlan(plan, do.cuda())
+    got = bp()
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.mask.row_ptr.cpu().numpy(), rp)
+    got = [t[:, sel] for t in got]
+    scale = 1.0 / math.sqrt(w["d"])
+    qs, ks, vs, ds = [f64(t[:, sel]) for t in (q, k, v, do)]
+    ref = ob.csr_attention_bwd(qs, ks, vs, ds, rp, ci, w["block"], True, scale, mags=True)
+    _check_all(got, ref, torch.bfloat16, "long-context full size")

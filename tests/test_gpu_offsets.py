@@ -18,8 +18,17 @@ pytestmark = pytest.mark.gpu
 W = wl.OFFSET_WORKLOAD
 
 
+def _tables(Wn, alpha, N):
+    """(table the kernel gets, table the oracle uses): the product's own table
+    builder feeds the kernel, as in the bench; the reference output is computed
+    over the oracle's table, so a difference between the two shows up as a
+    parity failure."""
+    return (api.offset_attn_make_table(Wn, alpha, api.fibonacci_base(N), N),
+            oo.offset_table(Wn, alpha, oo.fibonacci_base(N), N))
+
+
 def _table(alpha, N):
-    return oo.offset_table(W["W"], alpha, oo.fibonacci_base(N), N)
+    return _tables(W["W"], alpha, N)
 
 
 @pytest.mark.parametrize("N", W["lengths"])
@@ -27,12 +36,12 @@ def test_all_alphas_reduced_batch(N):
     require_gpu()
     B, H = 1, 2
     for l, alpha in enumerate(W["alphas"]):
-        offs = _table(alpha, N)
+        offs, offs_ref = _table(alpha, N)
         q, k, v = wl.make_qkv(B, H, N, W["d"], torch.bfloat16, W["qkv_seed_base"][N] + l)
         announce(f"[offset] N={N} alpha={alpha:.4f} |D|={len(offs)}")
         o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
         torch.cuda.synchronize()
-        o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 1 / math.sqrt(W["d"]))
+        o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs_ref, 1 / math.sqrt(W["d"]))
         compare(o, lse, o_ref, l_ref, torch.bfloat16, f"N={N} l={l}")
 
 
@@ -45,12 +54,12 @@ def test_full_size_sampled(N):
                      {(R.randrange(B), R.randrange(H), R.randrange(N)) for _ in range(94)})
     for l in (0, 7, 15):
         alpha = W["alphas"][l]
-        offs = _table(alpha, N)
+        offs, offs_ref = _table(alpha, N)
         q, k, v = wl.make_qkv(B, H, N, d, torch.bfloat16, W["qkv_seed_base"][N] + l)
         announce(f"[offset] full {B}x{H}x{N}x{d} l={l}")
         o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
         torch.cuda.synchronize()
-        o_ref, l_ref = oo.offset_attention_rows(f64(q), f64(k), f64(v), offs, 1 / math.sqrt(d), samples)
+        o_ref, l_ref = oo.offset_attention_rows(f64(q), f64(k), f64(v), offs_ref, 1 / math.sqrt(d), samples)
         og = torch.stack([o[b, h, t] for b, h, t in samples])
         lg = torch.stack([lse[b, h, t] for b, h, t in samples])
         compare(og, lg, o_ref, l_ref, torch.bfloat16, f"full N={N} l={l}")
@@ -61,12 +70,12 @@ def test_full_size_sampled(N):
 def test_ragged_lengths_and_dtypes(dtype, d):
     require_gpu()
     for N in (1, 63, 257, 1000):
-        offs = oo.offset_table(5, 1.3, oo.fibonacci_base(N), N)
+        offs, offs_ref = _tables(5, 1.3, N)
         q, k, v = wl.make_qkv(2, 2, N, d, dtype, 500 + N)
         announce(f"[offset] ragged N={N} d={d} {dtype}")
         o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs, 0.2)
         torch.cuda.synchronize()
-        o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 0.2)
+        o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs_ref, 0.2)
         compare(o, lse, o_ref, l_ref, dtype, f"ragged N={N}")
 
 
@@ -94,11 +103,11 @@ def test_full_table_is_dense_causal():
 def test_gqa_offsets():
     require_gpu()
     q, k, v = wl.make_qkv(2, 4, 512, 64, torch.bfloat16, 10, H_kv=1)
-    offs = _table(1.5, 512)
+    offs, offs_ref = _table(1.5, 512)
     announce("[offset] gqa")
     o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
     torch.cuda.synchronize()
-    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 0.125)
+    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs_ref, 0.125)
     compare(o, lse, o_ref, l_ref, torch.bfloat16, "gqa")
 
 
@@ -137,11 +146,11 @@ def test_strided_layout_and_negative_scale():
     g = torch.Generator().manual_seed(77)
     store = [torch.randn(B, N, H, d, generator=g).to(torch.bfloat16) for _ in range(3)]
     q, k, v = [t.cuda().permute(0, 2, 1, 3) for t in store]
-    offs = _table(1.7, N)
+    offs, offs_ref = _table(1.7, N)
     announce("[offset] strided [B,N,H,d] layout, scale -0.125")
     o, lse = api.offset_attn_fwd(q, k, v, offs, -0.125)
     torch.cuda.synchronize()
-    o_ref, l_ref = oo.offset_attention(f64(q.cpu()), f64(k.cpu()), f64(v.cpu()), offs, -0.125)
+    o_ref, l_ref = oo.offset_attention(f64(q.cpu()), f64(k.cpu()), f64(v.cpu()), offs_ref, -0.125)
     compare(o, lse, o_ref, l_ref, torch.bfloat16, "strided")
 
 
@@ -151,10 +160,10 @@ def test_multi_tile_walk_ragged():
     last walk of every head is shorter."""
     require_gpu()
     B, H, N, d = 4, 24, 4100, 64
-    offs = _table(1.25, N)
+    offs, offs_ref = _table(1.25, N)
     q, k, v = wl.make_qkv(B, H, N, d, torch.bfloat16, 4100)
     announce(f"[offset] multi-tile walk {B}x{H}x{N}x{d}")
     o, lse = api.offset_attn_fwd(q.cuda(), k.cuda(), v.cuda(), offs)
     torch.cuda.synchronize()
-    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs, 1 / math.sqrt(d))
+    o_ref, l_ref = oo.offset_attention(f64(q), f64(k), f64(v), offs_ref, 1 / math.sqrt(d))
     compare(o, lse, o_ref, l_ref, torch.bfloat16, "walk")

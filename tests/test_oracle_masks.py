@@ -23,6 +23,51 @@ def _spec(nb, **kw):
 
 # ---------------------------------------------------------------- RNG ----
 
+def read_rng_vectors():
+    """(keys, literals, draws) of tests/golden/rng_vectors.txt."""
+    keys, lits, draws = [], [], []
+    for line in open(golden_path("rng_vectors.txt")):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "key":
+            keys.append((tuple(int(x, 0) for x in f[1:6]), int(f[6], 16)))
+        elif f[0] == "lit":
+            lits.append(((int(f[1], 0), int(f[2], 0), int(f[3], 0), float(f[4])), int(f[5])))
+        elif f[0] == "draw":
+            want = [] if f[6] == "-" else [int(x) for x in f[6].split(",")]
+            draws.append((tuple(int(x, 0) for x in f[1:6]), want))
+    return keys, lits, draws
+
+
+def test_rng_known_answer_vectors():
+    """The frozen key chain, Bernoulli and distinct-draw vectors (the RNG
+    convention of the masks; the same file pins the library's host path)."""
+    keys, lits, draws = read_rng_vectors()
+    assert len(keys) == 10 and len(lits) == 36 and len(draws) == 10
+    for (s, t, a, b, c), want in keys:
+        assert rng.draw_key(s, t, a, b, c) == want
+    for (s, g, j, p), want in lits:
+        assert rng.literal_flag(s, g, j, p) == want
+    for (s, g, i, n, r), want in draws:
+        assert rng.random_blocks(s, g, i, n, r) == want
+
+
+def test_rng_key_chain_structure():
+    """key(seed, tag, a, b, c) is SplitMix64 applied five times, each time to
+    the previous output xor the next word: with every word 0 it is the
+    five-fold composition from sm(seed); the published first output of a
+    generator seeded with 0 (sm(0)) starts the chain of seed 0."""
+    sm0 = [int(x, 16) for x in open(golden_path("splitmix64_seed0.txt")) if x.strip() and not x.startswith("#")][0]
+    assert rng.splitmix64(0) == sm0
+    h = sm0
+    for _ in range(4):
+        h = rng.splitmix64(h)
+    assert rng.draw_key(0, 0, 0, 0, 0) == h
+    # each word enters by xor right after the output it follows
+    assert rng.draw_key(0, 1, 0, 0, 0) == rng.splitmix64(rng.splitmix64(rng.splitmix64(rng.splitmix64(sm0 ^ 1))))
+
+
 def test_splitmix64_known_answers():
     vals = [int(x, 16) for x in open(golden_path("splitmix64_seed0.txt"))
             if x.strip() and not x.startswith("#")]
