@@ -261,6 +261,31 @@ sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k, const voi
                           int32_t split_ways, void* workspace, int64_t workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * sparse_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the split-row
+ * workspace is a static device array of SA_NOALLOC_SCRATCH_BYTES held by every
+ * device the library runs on until the process ends.  Arguments, results and
+ * errors as for sparse_attn_fwd (workspace and workspace_bytes left out), plus
+ * SA_ERR_CAPACITY when sparse_attn_fwd_workspace_bytes(B, H, d, block,
+ * split_rows, split_ways) exceeds SA_NOALLOC_SCRATCH_BYTES (for example the
+ * BigBird workload's split, 2 rows x 8 ways of 24 heads at d = 64, needs
+ * 6.8 MB).  With split_rows > 0 (bf16) each call first zeroes the arrival
+ * counters it uses with a small kernel on `stream`, then launches the
+ * forward.  All calls on one device share its array: calls that overlap in
+ * time on one device (other streams, other threads) race and must not be
+ * issued; calls with split_rows = 0 or fp32 touch no scratch.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES (16 << 20)
+sa_status sparse_attn_fwd_noalloc(int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                                  float* lse, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
+                                  int32_t block, const int64_t* strides, const int32_t* row_ptr,
+                                  const int32_t* col_idx, int64_t col_capacity, const int32_t* sched,
+                                  int32_t num_groups, int64_t mask_batch_stride, int64_t mask_head_stride,
+                                  int32_t causal, float scale, int32_t row_split, int32_t split_rows,
+                                  int32_t split_ways, hipStream_t stream);
+
 /* Bytes of the split-row workspace of sparse_attn_fwd: 0 when split_rows = 0,
  * else 4 * SA_SPLIT_COUNTERS bytes of counters followed by the partial
  * states; SA_ERR_INVALID / SA_ERR_UNSUPPORTED (negative) for invalid sizes

@@ -38,6 +38,7 @@ SA_MAX_PERIOD = 64
 SA_MAX_RUNGS = 64
 SA_MAX_SPLIT_WAYS = 16
 SA_SPLIT_COUNTERS = 16384
+SA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # every function the header declares, with (restype, argtypes)
 _i32, _i64, _f32, _f64, _u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_uint64
@@ -74,6 +75,9 @@ SIGNATURES = {
                                ctypes.POINTER(_i64), _p, _p, _i64, _p, _i32, _i64, _i64, _i32,
                                _f32, _i32, _i32, _i32, _p, _i64, _p]),
     "sparse_attn_fwd_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "sparse_attn_fwd_noalloc": (_i32, [_i32, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       ctypes.POINTER(_i64), _p, _p, _i64, _p, _i32, _i64, _i64, _i32,
+                                       _f32, _i32, _i32, _i32, _p]),
     "sparse_attn_literal_flags": (_i32, [_p, _i32, _i64, _i32, _i32, _p, _p]),
     "offset_attn_make_table": (_i32, [_i32, _f64, ctypes.POINTER(_i64), _i32, _i32,
                                       ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),

@@ -271,6 +271,29 @@ def sparse_attn_fwd(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_st
     return o, lse_t
 
 
+def sparse_attn_fwd_noalloc(q, k, v, mask, scale=None, mask_batch_stride=0, mask_head_stride=0,
+                            use_schedule=True, out=None, lse=None, row_split=1, split_rows=0, split_ways=2):
+    """sparse_attn_fwd through the entry point that allocates nothing on the
+    device (its split-row workspace is the library's static scratch);
+    returns (o, lse).  Pass ``out`` and ``lse`` to allocate nothing here
+    either."""
+    B, H, Hkv, N, d = _check_qkv(q, k, v)
+    if N % mask.num_blocks:
+        raise ValueError("N must be a multiple of the number of mask blocks")
+    block = N // mask.num_blocks
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    sched = mask.sched if use_schedule else None
+    st = L.lib().sparse_attn_fwd_noalloc(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, block,
+        _strides(q, k, v, o), _ptr(mask.row_ptr), _ptr(mask.col_idx), mask.col_idx.numel(),
+        _ptr(sched), mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal),
+        scale, int(row_split), int(split_rows), int(split_ways), _stream(q.device))
+    _check(st, "sparse_attn_fwd_noalloc")
+    return o, lse_t
+
+
 def sparse_attn_mask_transpose(mask):
     """(col_ptr int32 [G*N_b+1], row_idx int32 [capacity]) device tensors: for
     each key block the ascending query blocks whose row lists it."""

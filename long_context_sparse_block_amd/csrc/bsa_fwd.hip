@@ -32,6 +32,7 @@
 // fp32 path: a plain VALU kernel, one thread per query, for exact checks.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "sa_device.h"
@@ -914,6 +915,41 @@ sa_status fwd_launch(const BsaArgs& a, int32_t dtype, int32_t d, int32_t block, 
   return launch(bsa_fwd_f32_kernel<128, 128>, a, 128, 0, stream, "bsa_fwd_f32<128,128>");
 }
 
+// Scratch of sparse_attn_fwd_noalloc: the split-row workspace of callers that
+// cannot allocate.  Every device holds its own copy until the process ends;
+// host code reaches it only through the address hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in).
+static __device__ __align__(256) uint8_t scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device).
+sa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return sa_host::record_hip_error(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return SA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return sa_host::record_hip_error(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return SA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+// Sets n int32 to zero (a kernel rather than a memset, so that the call can
+// sit in a captured graph).
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* p, int32_t n) {
+  const int32_t x = blockIdx.x * 256 + threadIdx.x;
+  if (x < n) p[x] = 0;
+}
+
 }  // namespace
 
 extern "C" int64_t sparse_attn_fwd_workspace_bytes(int32_t B, int32_t H, int32_t d, int32_t block,
@@ -939,5 +975,41 @@ extern "C" sa_status sparse_attn_fwd(int32_t dtype, const void* q, const void* k
                                  col_capacity, sched, num_groups, mask_batch_stride, mask_head_stride, causal,
                                  scale, row_split, split_rows, split_ways, workspace, workspace_bytes, a);
   if (st != SA_OK) return st;
+  return fwd_launch(a, dtype, d, block, row_split, stream);
+}
+
+extern "C" sa_status sparse_attn_fwd_noalloc(int32_t dtype, const void* q, const void* k, const void* v,
+                                             void* o, float* lse, int32_t B, int32_t H, int32_t H_kv,
+                                             int32_t N, int32_t d, int32_t block, const int64_t* strides,
+                                             const int32_t* row_ptr, const int32_t* col_idx,
+                                             int64_t col_capacity, const int32_t* sched, int32_t num_groups,
+                                             int64_t mask_batch_stride, int64_t mask_head_stride,
+                                             int32_t causal, float scale, int32_t row_split,
+                                             int32_t split_rows, int32_t split_ways, hipStream_t stream) {
+  const bool uses = dtype == SA_BF16 && split_rows > 0;
+  if (uses) {
+    const int64_t need = sparse_attn_fwd_workspace_bytes(B, H, d, block, split_rows, split_ways);
+    if (need > SA_NOALLOC_SCRATCH_BYTES) return SA_ERR_CAPACITY;
+  }
+  // every argument is checked before the scratch is looked up or anything is
+  // launched (a placeholder address stands in for the scratch while checking)
+  BsaArgs a;
+  sa_status st = fwd_setup(dtype, q, k, v, o, lse, B, H, H_kv, N, d, block, strides, row_ptr, col_idx,
+                           col_capacity, sched, num_groups, mask_batch_stride, mask_head_stride, causal, scale,
+                           row_split, split_rows, split_ways, uses ? (void*)(uintptr_t)256 : nullptr,
+                           SA_NOALLOC_SCRATCH_BYTES, a);
+  if (st != SA_OK) return st;
+  if (uses) {
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != SA_OK) return st;
+    a.split_cnt = (int32_t*)ws;
+    a.split_part = (float*)((uint8_t*)ws + split_layout(B, H, d, block, a.split_rows, a.split_ways).part);
+    // the counters this launch uses start at zero whatever an earlier call left
+    const int32_t n = B * H * a.split_rows;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.split_cnt, n);
+    st = sa_host::check_launch("zero_i32_kernel");
+    if (st != SA_OK) return st;
+  }
   return fwd_launch(a, dtype, d, block, row_split, stream);
 }

@@ -404,3 +404,21 @@ def test_library_rng_matches_oracle_on_workloads(lib):
     assert lib.sa_rng_random_blocks(1, 0, 0, 4, 2, None) == L.SA_ERR_NULL
     assert lib.sa_rng_random_blocks(1, 0, 0, -1, 2, out) == L.SA_ERR_INVALID
     assert lib.sa_rng_random_blocks(1, 0, 0, 4, L.SA_MAX_RANDOM + 1, out) == L.SA_ERR_INVALID
+
+
+def test_noalloc_rejects_oversized_split_before_anything(lib):
+    """sparse_attn_fwd_noalloc refuses a split whose workspace exceeds its
+    static scratch with SA_ERR_CAPACITY, and bad arguments as sparse_attn_fwd
+    does, on the host (fake device pointers are never touched)."""
+    fake = ctypes.c_void_p(1 << 20)
+    def call(**kw):
+        a = dict(dtype=L.SA_BF16, B=1, H=16, N=8192, d=128, block=128, split_rows=64, split_ways=16, causal=1)
+        a.update(kw)
+        return lib.sparse_attn_fwd_noalloc(a["dtype"], fake, fake, fake, fake, fake, a["B"], a["H"], a["H"], a["N"],
+                                           a["d"], a["block"], None, fake, fake, 1 << 20, None, 1, 0, 0, a["causal"],
+                                           0.1, 1, a["split_rows"], a["split_ways"], None)
+    assert lib.sparse_attn_fwd_workspace_bytes(1, 16, 128, 128, 64, 16) > L.SA_NOALLOC_SCRATCH_BYTES
+    assert call() == L.SA_ERR_CAPACITY
+    assert call(split_ways=1) == L.SA_ERR_INVALID
+    assert call(causal=2, split_rows=0) == L.SA_ERR_INVALID
+    assert call(d=96, split_rows=0) == L.SA_ERR_UNSUPPORTED
