@@ -24,8 +24,9 @@
 //     the accumulator to the operand registers with one bf16 pack and no LDS
 //     round trip.  The V^T operand comes from row-major V in LDS through
 //     transpose reads (ds_read_b64_tr_b16);
-//   * 16-byte LDS chunks are XOR-swizzled so the MFMA operand reads are free of
-//     bank conflicts;
+//   * 16-byte LDS chunks are XOR-swizzled so that the K operand reads
+//     (ds_read_b128, sa::lds_slot) and the V^T transpose reads
+//     (sa::lds_slot_tr) are free of bank conflicts on gfx950's 64-bank LDS;
 //   * launch order follows `sched` (longest rows first); blockIdx % (B*H) picks
 //     the head, so with B*H a multiple of 8 every query block of one head runs
 //     on the same XCD and shares its L2.
@@ -154,11 +155,6 @@ __device__ __forceinline__ void wait_vm_units(int c) {
   }
 }
 
-// 16-byte chunk position inside a K row: XOR with the key's low bits so the
-// 32 rows read by one MFMA operand load fall into distinct bank groups.
-__device__ __forceinline__ int swz_k(int c, int key) { return c ^ (key & 7); }
-// ... and inside a V row, matched to the 4-row groups of the transpose read.
-__device__ __forceinline__ int swz_v(int c, int key) { return c ^ ((key & 3) << 1); }
 
 // Software-pipeline shape: K operand k-steps read ahead, VALU instructions
 // scheduled after each S(n+1) MFMA.
@@ -265,21 +261,27 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
 
   // DMA plan: copy j of wave wq of a group moves chunks [64 (j QW + wq), +64)
   // of the group's K (or V) tile, i.e. whole rows (RPC rows per copy); lane i
-  // lands at 16 i past the copy's LDS base.  Copy j reads rows RPC j further
-  // down than copy 0, with the same swizzle (RPC is a multiple of 8), so one
-  // per-lane source offset serves every copy.  When the rows of a tile are
-  // contiguous in global memory (sequence stride = d) and copies j, j + 1 are
-  // 2048 bytes apart in both spaces, they share one M0 setup.
+  // lands at 16 i past the copy's LDS base and reads the global chunk that
+  // belongs in that slot (sa::lds_slot is its own inverse).  Copy j reads rows
+  // RPC j further down than copy 0; when RPC is a multiple of the slot
+  // pattern's period one per-lane source offset serves every copy, otherwise
+  // (RPC = 8: d = 128 with 64-query blocks) odd copies take a second one.
+  // When the rows of a tile are contiguous in global memory (sequence stride =
+  // d) and copies j, j + 1 are 2048 bytes apart in both spaces with one
+  // offset, they share one M0 setup.
   constexpr int RPC = C::QW * 64 / C::CPR;  // rows per copy
-  static_assert(RPC % 8 == 0, "copies must keep the row swizzle");
-  uint32_t offK, offV;
+  static_assert(RPC % 8 == 0, "copies hold whole rows");
+  constexpr bool kOddSlots = RPC % sa::kSlotPeriod != 0;
+  uint32_t offK, offV, offK1, offV1;
   {
     const int r = wq * 64 + lane;  // chunk of this lane in copy 0
     const int key = r / C::CPR, cs = r % C::CPR;
-    offK = (uint32_t)(key * ks2 * 2) + 16u * (uint32_t)swz_k(cs, key);
-    offV = (uint32_t)(key * vs2 * 2) + 16u * (uint32_t)swz_v(cs, key);
+    offK = (uint32_t)(key * ks2 * 2) + 16u * (uint32_t)sa::lds_slot<D>(cs, key);
+    offV = (uint32_t)(key * vs2 * 2) + 16u * (uint32_t)sa::lds_slot_tr<D>(cs, key);
+    offK1 = kOddSlots ? (uint32_t)(key * ks2 * 2) + 16u * (uint32_t)sa::lds_slot<D>(cs, key + RPC) : offK;
+    offV1 = offV;  // the V pattern repeats every 4 rows
   }
-  constexpr bool kPairs = C::QW * 64 * 16 == 2048 && C::JN % 4 == 0;
+  constexpr bool kPairs = C::QW * 64 * 16 == 2048 && C::JN % 4 == 0 && !kOddSlots;
   const bool k_contig = kPairs && ks2 == D, v_contig = kPairs && vs2 == D;
   const uint32_t kring = sa::lds_addr(smem) + grp * C::KVB;
   const uint32_t vring = kring + C::VRING;
@@ -291,8 +293,8 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
   // sequence strides), so a 32 x 32-bit product locates the tile.
   const uint32_t kbs = (uint32_t)(BLK * ks2 * 2), vbs = (uint32_t)(BLK * vs2 * 2);  // bytes per key block
   const uint32_t offK4 = offK + 4096u, offV4 = offV + 4096u;
-  auto dma_tile = [&](const uint16_t* X, uint32_t xbs, int64_t xs2, uint32_t off, uint32_t off4, bool contig,
-                      uint32_t ring, int slot, int32_t kb, int sub) {
+  auto dma_tile = [&](const uint16_t* X, uint32_t xbs, int64_t xs2, uint32_t off, uint32_t off1, uint32_t off4,
+                      bool contig, uint32_t ring, int slot, int32_t kb, int sub) {
     const char* src = (const char*)X + (uint64_t)(uint32_t)kb * xbs + (uint32_t)(sub * 64 * xs2 * 2);
     const uint32_t dst = ring + slot * C::SLOTB + wq * 64 * 16;
     if (contig) {  // pairs 2048 bytes apart, two pairs per M0 save
@@ -301,7 +303,7 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < C::JN; ++j)
-        sa::dma16(src + (uint64_t)j * RPC * xs2 * 2, off, dst + j * C::QW * 64 * 16);
+        sa::dma16(src + (uint64_t)j * RPC * xs2 * 2, (j & 1) ? off1 : off, dst + j * C::QW * 64 * 16);
     }
   };
 
@@ -333,15 +335,15 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
     };
     auto tile_sub = [&](int m) -> int { return C::SUBS == 1 ? 0 : min(m * np + gs, T - 1) % C::SUBS; };
     auto dma_k = [&](int m, int32_t kb, int slot) {
-      dma_tile(K, kbs, ks2, offK, offK4, k_contig, kring, slot, kb < 0 ? it.i : kb, tile_sub(m));
+      dma_tile(K, kbs, ks2, offK, offK1, offK4, k_contig, kring, slot, kb < 0 ? it.i : kb, tile_sub(m));
     };
     auto dma_v = [&](int m, int32_t kb, int slot) {
-      dma_tile(V, vbs, vs2, offV, offV4, v_contig, vring, slot, kb < 0 ? it.i : kb, tile_sub(m));
+      dma_tile(V, vbs, vs2, offV, offV1, offV4, v_contig, vring, slot, kb < 0 ? it.i : kb, tile_sub(m));
     };
     // K operand of S^T = K Q^T for k-step k: 32 keys (kt) x 16 dims.
     auto k_operand = [&](const uint8_t* ks, int k, int kt) -> sa::u32x4 {
       const int key = 32 * kt + lq;
-      return *(const sa::u32x4*)(ks + key * C::ROWB + swz_k(2 * k + hl, key) * 16);
+      return *(const sa::u32x4*)(ks + key * C::ROWB + sa::lds_slot<D>(2 * k + hl, key) * 16);
     };
 
     auto qk = [&](const uint8_t* ks, sa::f32x16(&dst)[2]) {
@@ -529,8 +531,8 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
         for (int u = 0; u < 4; ++u) {
           const int keyA = 16 * u + 4 * hl + (ii >> 2);
           const int keyB = keyA + 8;
-          const sa::u32x2 l2 = sa::lds_read_tr16(vs + keyA * C::ROWB + swz_v(cs, keyA) * 16 + half * 8);
-          const sa::u32x2 h2 = sa::lds_read_tr16(vs + keyB * C::ROWB + swz_v(cs, keyB) * 16 + half * 8);
+          const sa::u32x2 l2 = sa::lds_read_tr16(vs + keyA * C::ROWB + sa::lds_slot_tr<D>(cs, keyA) * 16 + half * 8);
+          const sa::u32x2 h2 = sa::lds_read_tr16(vs + keyB * C::ROWB + sa::lds_slot_tr<D>(cs, keyB) * 16 + half * 8);
           const sa::u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
           oacc[dt] = sa::mfma32(av, pb[u], oacc[dt]);
         }

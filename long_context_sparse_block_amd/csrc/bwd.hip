@@ -357,8 +357,10 @@ __global__ __launch_bounds__(BLK) void bsa_bwd_dkdv_f32(BwdArgs a) {
 // transposed from LDS with two ds_read_b64_tr_b16 (rows 16s + 4(l/32) + m and
 // 16s + 8 + 4(l/32) + m).
 
-// 16-byte chunk slot of a tile row in LDS (XOR of the row's low 3 bits)
-__device__ __forceinline__ int bswz(int c, int row) { return c ^ (row & 7); }
+// 16-byte chunk slot of a tile row in LDS: sa::lds_slot, conflict-free for
+// both the row reads (ds_read_b128) and the transpose reads below.
+template <int D>
+__device__ __forceinline__ int bswz(int c, int row) { return sa::lds_slot<D>(c, row); }
 
 template <int D>
 struct TileLds {
@@ -366,7 +368,13 @@ struct TileLds {
   // A operand of rows [r0, r0 + 32), d-chunks 2u + l/32 (16 d per k-step u)
   static __device__ __forceinline__ sa::u32x4 rows_a(const uint8_t* t, int r0, int u, int lane) {
     const int row = r0 + (lane & 31);
-    return *(const sa::u32x4*)(t + row * ROWB + bswz(2 * u + (lane >> 5), row) * 16);
+    return *(const sa::u32x4*)(t + row * ROWB + bswz<D>(2 * u + (lane >> 5), row) * 16);
+  }
+  // the same from an LDS byte address
+  static __device__ __forceinline__ sa::u32x4 rows_a_lds(uint32_t t, int r0, int u, int lane) {
+    const int row = r0 + (lane & 31);
+    typedef __attribute__((address_space(3))) const sa::u32x4* lptr;
+    return *(lptr)(uintptr_t)(t + row * ROWB + bswz<D>(2 * u + (lane >> 5), row) * 16);
   }
   // transposed A operand: d rows 32 dt + l%32, k = tile rows 16 s + 8(e/4) + 4(l/32) + e%4
   static __device__ __forceinline__ sa::u32x4 rows_tr(const uint8_t* t, int r0, int s, int dt, int lane) {
@@ -374,32 +382,42 @@ struct TileLds {
     const int d0 = 32 * dt + 16 * (grp & 1) + 4 * (p & 3);  // first d of the lane's 8-byte word
     const int ra = r0 + 16 * s + 4 * h + (p >> 2), rb = ra + 8;
     const int ca = d0 >> 3, half = (d0 & 7) * 2;
-    const sa::u32x2 x = sa::lds_read_tr16(t + ra * ROWB + bswz(ca, ra) * 16 + half);
-    const sa::u32x2 y = sa::lds_read_tr16(t + rb * ROWB + bswz(ca, rb) * 16 + half);
+    const sa::u32x2 x = sa::lds_read_tr16(t + ra * ROWB + bswz<D>(ca, ra) * 16 + half);
+    const sa::u32x2 y = sa::lds_read_tr16(t + rb * ROWB + bswz<D>(ca, rb) * 16 + half);
     return sa::u32x4{x[0], x[1], y[0], y[1]};
   }
 };
 
 // Direct (DMA) copies of one 64-row bf16 tile into a swizzled LDS tile.  Wave
 // w of NW issues JN copies of 64 16-byte chunks; chunk u = 64 (j NW + w) + lane
-// of copy j is row u / CPR, slot u % CPR, so one per-lane source offset (row
-// r0 = (64 w + lane) / CPR, logical chunk slot ^ (r0 & 7)) serves every copy:
-// copy j reads RPC j rows further down (RPC a multiple of 8 keeps the swizzle)
-// and lands j NW KiB further into the tile.
+// of copy j is row u / CPR, slot u % CPR, and lane `lane` reads the global
+// chunk that belongs in that slot.  Copy j reads RPC j rows further down and
+// lands j NW KiB further into the tile; when RPC is a multiple of the slot
+// pattern's period one per-lane source offset serves every copy, otherwise
+// (RPC = 8: d = 128 with two waves) odd copies take a second offset.
 template <int D, int NW>
 struct TileDma {
   static constexpr int CPR = D / 8;
   static constexpr int JN = CPR / NW;         // copies per wave per tile
   static constexpr int RPC = NW * 64 / CPR;   // rows between a wave's copies
   static constexpr int TB = 64 * 2 * D;       // bytes of one tile
+  static constexpr bool ODD = RPC % sa::kSlotPeriod != 0;
   static_assert(JN >= 1 && RPC % 8 == 0, "tile split");
-  static __device__ __forceinline__ uint32_t lane_off(int w, int lane, int64_t rs) {
+  struct Off {
+    uint32_t even, odd;
+  };
+  static __device__ __forceinline__ Off lane_off(int w, int lane, int64_t rs) {
     const int r0 = (64 * w + lane) / CPR, p = lane % CPR;
-    return (uint32_t)(r0 * rs * 2) + 16u * (uint32_t)(p ^ (r0 & 7));
+    const uint32_t row = (uint32_t)(r0 * rs * 2);
+    Off o;
+    o.even = row + 16u * (uint32_t)bswz<D>(p, r0);
+    o.odd = ODD ? row + 16u * (uint32_t)bswz<D>(p, r0 + RPC) : o.even;
+    return o;
   }
-  static __device__ __forceinline__ void copy(const uint16_t* src, int64_t rs, uint32_t off, uint32_t lds, int w) {
+  static __device__ __forceinline__ void copy(const uint16_t* src, int64_t rs, Off off, uint32_t lds, int w) {
 #pragma unroll
-    for (int j = 0; j < JN; ++j) sa::dma16((const char*)src + (int64_t)j * RPC * rs * 2, off, lds + (j * NW + w) * 1024);
+    for (int j = 0; j < JN; ++j)
+      sa::dma16((const char*)src + (int64_t)j * RPC * rs * 2, (j & 1) ? off.odd : off.even, lds + (j * NW + w) * 1024);
   }
 };
 
@@ -511,7 +529,7 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
   sa::f32x16 acc[NT];
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::f32x16{};
-  const uint32_t offK = M::lane_off(w, lane, ks2), offV = M::lane_off(w, lane, vs2);
+  const typename M::Off offK = M::lane_off(w, lane, ks2), offV = M::lane_off(w, lane, vs2);
   const uint32_t ring = sa::lds_addr(smem);
   int32_t e0, e1;
   row_range(a, g, i, e0, e1);
@@ -656,20 +674,8 @@ __global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
   }
 }
 
-// d = 128: SA_BWD_DKDV_DSPLIT waves per 32 keys, each recomputing S and dP and
-// holding 1 / DSPLIT of the dK, dV accumulators.  The full set needs more than
-// 256 registers (one wave per SIMD); two waves per SIMD with the split measured
-// slower on the long-context workload (7.04 vs 6.71 ms), so the default is 1.
-#ifndef SA_BWD_DKDV_DSPLIT
-#define SA_BWD_DKDV_DSPLIT 1
-#endif
-template <int D>
-struct DkdvCfg {
-  static constexpr int DS = D == 128 ? SA_BWD_DKDV_DSPLIT : 1;
-};
-
-// dk, dv: persistent workgroups (BLK/32 * DS waves, DS waves per 32 keys of
-// the key block) take work items = chunks of columns: entries [chunk * C, chunk * C +
+// dk, dv: persistent workgroups (BLK/32 waves, one per 32 keys of the key
+// block) take work items = chunks of columns: entries [chunk * C, chunk * C +
 // C) of the column's list (C <= 64), so that a key block listed by many query
 // blocks (a global block) is shared by several workgroups.  A column with
 // one chunk writes its bf16 rows directly; the chunks of a split column add
@@ -678,20 +684,28 @@ struct DkdvCfg {
 // The item's query blocks (and their q heads) are held in VGPR lanes; their
 // 64-row tiles of Q and dO, with the rows' {lse log2(e), D} pairs, are copied
 // global -> LDS by direct loads into a ring of S slots (tile n + S - 1 in
-// flight while tile n is used).  Wave 0 copies the tile's row statistics,
-// which every wave reads after the ring barrier.
-template <int D, int BLK, int S>
-__global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(BwdArgs a) {
+// flight while tile n is used; with one slot the next tile is copied once
+// every wave has read the current one).  Wave 0 copies the tile's row
+// statistics, which every wave reads after the ring barrier.
+//
+// The key block's K rows are the B operand of S = Q K^T and stay in registers.
+// Its V rows, the B operand of dP = dO V^T, stay in registers too (VL false),
+// or (VL true: d = 128, where keeping both takes more than 256 registers, one
+// wave per SIMD) are copied once per item into LDS and read back at every use,
+// next to a one-slot Q / dO ring: 65 KiB of LDS at block 128, at most 256
+// registers, two waves per SIMD.
+template <int D, int BLK, int S, bool VL>
+__global__ __launch_bounds__(2 * BLK) __attribute__((amdgpu_waves_per_eu(VL ? 2 : 1)))
+void bsa_bwd_dkdv_bf16(BwdArgs a) {
   using L = TileLds<D>;
-  constexpr int DS = DkdvCfg<D>::DS;  // waves per 32 keys, each holding NT / DS of the dK, dV tiles
-  constexpr int NW = BLK / 32 * DS, NU = D / 16, NT = D / 32, NTW = NT / DS, SUBS = BLK / 64;
+  constexpr int NW = BLK / 32, NU = D / 16, NT = D / 32, SUBS = BLK / 64;
   using M = TileDma<D, NW>;
   constexpr int SLOT = 2 * M::TB + 1024;  // Q tile, dO tile, the rows' statistics
   constexpr int CP = 2 * M::JN;           // tile copies per wave per tile (wave 0: + 1)
-  static_assert(S == 2 || S == 3, "ring slots");
+  static_assert(S == 2 || S == 3 || (S == 1 && VL), "ring slots");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
-  const int kg = w / DS, dh = w % DS;  // key group (32 keys) and d part of this wave
+  const int kg = w;  // key group (32 keys) of this wave
   const int32_t rep = a.H / a.H_kv;
   const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
   const int32_t items = a.pre[cols];
@@ -699,6 +713,7 @@ __global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(Bw
   // long ones, started first); item extra + c is the first chunk of column c.
   const int32_t extra = items - (int32_t)cols;
   const uint32_t ring = sa::lds_addr(smem);
+  const uint32_t vblk = ring + S * SLOT;  // V rows of the key block (VL)
   const uint32_t soff = 16u * (uint32_t)(lane & 31);  // statistics: 2 rows per lane, lanes 32.. repeat
   bool first = true;
   for (int32_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -731,11 +746,11 @@ __global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(Bw
     const int64_t sk = (int64_t)j * BLK + koff;   // ... and in the sequence (C column)
     const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
     const uint16_t* V = (const uint16_t*)a.v + b * a.st[TV][0] + kvh * a.st[TV][1];
-    sa::u32x4 kb_[NU], vb_[NU];  // B operands: column = key, k = d
+    sa::u32x4 kb_[NU], vb_[VL ? 1 : NU];  // B operands: column = key, k = d
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       kb_[u] = *(const sa::u32x4*)(K + sk * a.st[TK][2] + 16 * u + 8 * hl);
-      vb_[u] = *(const sa::u32x4*)(V + sk * a.st[TV][2] + 16 * u + 8 * hl);
+      if constexpr (!VL) vb_[u] = *(const sa::u32x4*)(V + sk * a.st[TV][2] + 16 * u + 8 * hl);
     }
     // the item's entries: flat entry f0 + x (over the heads in order) in lane x
     int32_t lq = -1, lh = 0, total = 0;
@@ -754,15 +769,18 @@ __global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(Bw
     // the loads above complete here, before any copy is in flight (stores of
     // the previous item included)
 #pragma unroll
-    for (int u = 0; u < NU; ++u) sa::keep(kb_[u]), sa::keep(vb_[u]);
+    for (int u = 0; u < NU; ++u) sa::keep(kb_[u]);
+    if constexpr (!VL)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) sa::keep(vb_[u]);
     sa::keep(lq), sa::keep(lh), sa::keep(split);
     sa::vm_wait<0>();
-    if (!first) ring_barrier();  // every wave is done with the ring
+    if (!first) ring_barrier();  // every wave is done with the ring (and the V rows)
     first = false;
 
-    sa::f32x16 dk[NTW], dv[NTW];  // d tiles dh NTW + t
+    sa::f32x16 dk[NT], dv[NT];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) dk[t] = sa::f32x16{}, dv[t] = sa::f32x16{};
+    for (int t = 0; t < NT; ++t) dk[t] = sa::f32x16{}, dv[t] = sa::f32x16{};
     const int T = cnt * SUBS;
     auto issue = [&](int m) {
       const int32_t qb = sa::readlane(lq, m / SUBS), h = sa::readlane(lh, m / SUBS);
@@ -775,73 +793,101 @@ __global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(Bw
       M::copy(G + r0 * a.st[TDO][2], a.st[TDO][2], M::lane_off(w, lane, a.st[TDO][2]), dst + M::TB, w);
       if (w == 0) sa::dma16(st, soff, dst + 2 * M::TB);
     };
+    if constexpr (VL) {
+      // the key block's V rows, 64-row tiles one after the other
+#pragma unroll
+      for (int sub = 0; sub < SUBS; ++sub)
+        M::copy(V + ((int64_t)j * BLK + 64 * sub) * a.st[TV][2], a.st[TV][2], M::lane_off(w, lane, a.st[TV][2]),
+                vblk + sub * M::TB, w);
+    }
     if (T > 0) issue(0);
     if (S > 2 && T > 1) issue(1);
     for (int n = 0; n < T; ++n) {
-      if (w == 0)
-        wait_units<CP + 1>(S > 2 && n + 1 < T);
-      else
-        wait_units<CP>(S > 2 && n + 1 < T);
-      ring_barrier();
-      if (n + S - 1 < T) issue(n + S - 1);
+      if constexpr (S == 1) {
+        sa::vm_wait<0>();
+        ring_barrier();
+      } else {
+        if (w == 0)
+          wait_units<CP + 1>(S > 2 && n + 1 < T);
+        else
+          wait_units<CP>(S > 2 && n + 1 < T);
+        ring_barrier();
+        if (n + S - 1 < T) issue(n + S - 1);
+      }
       const int32_t qb = sa::readlane(lq, n / SUBS);
-      if (qb < 0) continue;
-      const uint8_t* qs = smem + (n % S) * SLOT;
-      const uint8_t* gs = qs + M::TB;
-      const float* sts = (const float*)(gs + M::TB);
-      const int qsub = 64 * (n % SUBS);
-      const bool diag = a.causal && qb == j;
-      // one 32-query half; MASK: apply the causal triangle when diag
-      auto half = [&](int qt, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        // S and dP [32 queries x 32 keys]
-        sa::f32x16 s = {}, dp = {};
+      if (qb >= 0) {
+        const uint8_t* qs = smem + (n % S) * SLOT;
+        const uint8_t* gs = qs + M::TB;
+        const float* sts = (const float*)(gs + M::TB);
+        const int qsub = 64 * (n % SUBS);
+        const bool diag = a.causal && qb == j;
+        // one 32-query half; MASK: apply the causal triangle when diag
+        auto half = [&](int qt, auto mask_tag) {
+          constexpr bool MASK = decltype(mask_tag)::value;
+          // V rows of this wave's keys, read again for every half (the opaque
+          // base keeps the compiler from holding them in registers)
+          uint32_t vrows = vblk + (uint32_t)(32 * kg / 64) * M::TB;
+          asm volatile("" : "+s"(vrows));
+          // S and dP [32 queries x 32 keys]
+          sa::f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
-          dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vb_[u], dp);
-        }
-        float p[16], ds[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
-          const sa::f32x4 x0 = *(const sa::f32x4*)(sts + 2 * q4);  // {l, D} of rows q4, q4 + 1
-          const sa::f32x4 x1 = *(const sa::f32x4*)(sts + 2 * q4 + 4);
-          const float lv[4] = {x0[0], x0[2], x1[0], x1[2]}, dv4[4] = {x0[1], x0[3], x1[1], x1[3]};
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const int r = 4 * r4 + cc;
-            p[r] = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -lv[cc]));
-            // keys after the query
-            if (MASK && diag && koff > qsub + q4 + cc) p[r] = 0.f;
-            ds[r] = p[r] * (dp[r] - dv4[cc]);
+          for (int u = 0; u < NU; ++u) {
+            s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
+            sa::u32x4 vop;
+            if constexpr (VL)
+              vop = L::rows_a_lds(vrows, (32 * kg) % 64, u, lane);
+            else
+              vop = vb_[u];
+            dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vop, dp);
           }
-        }
-        // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
+          float p[16], ds[16];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int q4 = 32 * qt + 8 * r4 + 4 * hl;  // 4 consecutive query rows of the tile
+            const sa::f32x4 x0 = *(const sa::f32x4*)(sts + 2 * q4);  // {l, D} of rows q4, q4 + 1
+            const sa::f32x4 x1 = *(const sa::f32x4*)(sts + 2 * q4 + 4);
+            const float lv[4] = {x0[0], x0[2], x1[0], x1[2]}, dv4[4] = {x0[1], x0[3], x1[1], x1[3]};
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            const int dt = dh * NTW + t;
-            dv[t] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[t]);
-            dk[t] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[t]);
+            for (int cc = 0; cc < 4; ++cc) {
+              const int r = 4 * r4 + cc;
+              p[r] = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -lv[cc]));
+              // keys after the query
+              if (MASK && diag && koff > qsub + q4 + cc) p[r] = 0.f;
+              ds[r] = p[r] * (dp[r] - dv4[cc]);
+            }
           }
+          // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) {
+              dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
+              dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
+            }
+          }
+        };
+        bwd_tile<D>(diag, half);
+      }
+      if constexpr (S == 1) {
+        if (n + 1 < T) {
+          // every wave has read tile n (its LDS reads returned): refill the slot
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          ring_barrier();
+          issue(n + 1);
         }
-      };
-      bwd_tile<D>(diag, half);
+      }
     }
-    // C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's key
+// C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's key
     if (!split) {
       uint16_t* DK = (uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + sk * a.st[TDK][2];
       uint16_t* DV = (uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + sk * a.st[TDV][2];
 #pragma unroll
-      for (int t = 0; t < NTW; ++t)
+      for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int dt = dh * NTW + t;
-          const sa::f32x16& x = dk[t];
-          const sa::f32x16& y = dv[t];
+          const sa::f32x16& x = dk[dt];
+          const sa::f32x16& y = dv[dt];
           const int r = 4 * r4;
           *(sa::u32x2*)(DK + 32 * dt + 8 * r4 + 4 * hl) = sa::u32x2{
               sa::pack_bf16x2(x[r] * a.scale, x[r + 1] * a.scale), sa::pack_bf16x2(x[r + 2] * a.scale, x[r + 3] * a.scale)};
@@ -852,12 +898,12 @@ __global__ __launch_bounds__(2 * BLK * DkdvCfg<D>::DS) void bsa_bwd_dkdv_bf16(Bw
       const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
       float* pk = a.acc + ((int64_t)bk * a.N + sk) * D;
 #pragma unroll
-      for (int t = 0; t < NTW; ++t)
+      for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int x = 32 * (dh * NTW + t) + 8 * (r >> 2) + 4 * hl + (r & 3);
-          atomicAdd(pk + x, dk[t][r]);
-          atomicAdd(pk + plane + x, dv[t][r]);
+          const int x = 32 * dt + 8 * (r >> 2) + 4 * hl + (r & 3);
+          atomicAdd(pk + x, dk[dt][r]);
+          atomicAdd(pk + plane + x, dv[dt][r]);
         }
     }
   }
@@ -1153,23 +1199,19 @@ sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t s
 #define SA_BWD_CHUNK_TILES 64
 #endif
 
-// ring slots of the block-sparse bf16 dQ and dK/dV kernels
-#ifndef SA_BWD_DQ_SLOTS
-#define SA_BWD_DQ_SLOTS 2
-#endif
-#ifndef SA_BWD_DKDV_SLOTS
-#define SA_BWD_DKDV_SLOTS 2
-#endif
 
 template <int D, int BLK>
 sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
   const int64_t nq = (int64_t)a.B * a.H * a.nb, nk = (int64_t)a.B * a.H_kv * a.nb;
   sa_status st;
   if (bf16) {
-    constexpr int SQ = SA_BWD_DQ_SLOTS, SK = SA_BWD_DKDV_SLOTS;
+    // d = 128: the dK/dV kernel keeps V in LDS beside a one-slot ring (two
+    // waves per SIMD); d = 64: V in registers and a two-slot ring
+    constexpr int SQ = 2;
+    constexpr bool VL = D == 128;
+    constexpr int SK = VL ? 1 : 2;
     constexpr int lds_dq = SQ * 2 * TileDma<D, BLK / 32>::TB;
-    constexpr int DS = DkdvCfg<D>::DS;
-    constexpr int lds_kv = SK * (2 * TileDma<D, BLK / 32 * DS>::TB + 1024);
+    constexpr int lds_kv = SK * (2 * TileDma<D, BLK / 32>::TB + 1024) + (VL ? BLK * 2 * D : 0);
     st = launch(bsa_bwd_dq_bf16<D, BLK, SQ>, a, nq, 2 * BLK, lds_dq, stream, "bsa_bwd_dq_bf16");
     if (st != SA_OK) return st;
     const int64_t wblocks = (nk + 3) / 4;
@@ -1179,7 +1221,7 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     st = sa_host::check_launch("scan_kernel");
     if (st != SA_OK) return st;
     // persistent workgroups; the item count lives on the device
-    st = launch(bsa_bwd_dkdv_bf16<D, BLK, SK>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK * DS, lds_kv,
+    st = launch(bsa_bwd_dkdv_bf16<D, BLK, SK, VL>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK, lds_kv,
                 stream, "bsa_bwd_dkdv_bf16");
     if (st != SA_OK) return st;
     return launch(dkdv_convert_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_convert_kernel");

@@ -256,6 +256,36 @@ __device__ __forceinline__ void dma16x4(const void* sbase, uint32_t voff, uint32
 #endif
 }
 
+// Slot of 16-byte chunk c of a row of D bf16 values in an LDS tile (rows of
+// 2D bytes, stored back to back).  gfx950 reads LDS as 64 banks of 4 bytes:
+// ds_read_b128 serves 16 lanes per cycle and ds_read_b64_tr_b16 32 lanes.  The
+// XOR below makes both access patterns of the MFMA operands conflict-free:
+// 16 consecutive rows read at one logical chunk (b128), and 4 consecutive rows
+// (a multiple of 4 first) read at 4 consecutive chunks with both 8-byte halves
+// (transpose reads).  At D = 128 a row fills all 16 bank groups of 16 bytes,
+// so the 16 rows need 16 distinct slots; at D = 64 two rows share the 16
+// groups, so the slots of the 8 rows of each parity must differ.  The pattern
+// repeats every 16 rows.
+template <int D>
+__device__ __forceinline__ int lds_slot(int c, int row) {
+  static_assert(D == 64 || D == 128, "row width");
+  if constexpr (D == 128)
+    return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  else
+    return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+constexpr int kSlotPeriod = 16;  // rows after which lds_slot repeats
+
+// Slot pattern for a tile that is only read by transpose reads (4 consecutive
+// rows at 4 consecutive chunks): the row's two low bits spread the 4 rows over
+// distinct groups of slots.  Repeats every 4 rows, so rows 8 apart share their
+// offsets.
+template <int D>
+__device__ __forceinline__ int lds_slot_tr(int c, int row) {
+  static_assert(D == 64 || D == 128, "row width");
+  return c ^ ((row & 3) << (D == 128 ? 2 : 1));
+}
+
 // LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
