@@ -158,12 +158,8 @@ __device__ __forceinline__ void wait_vm_units(int c) {
 
 // Software-pipeline shape: K operand k-steps read ahead, VALU instructions
 // scheduled after each S(n+1) MFMA.
-#ifndef SA_KPRE
-#define SA_KPRE 4
-#endif
-#ifndef SA_VGROUP
-#define SA_VGROUP 12
-#endif
+constexpr int kKPre = 4;
+constexpr int kVGroup = 12;
 
 template <int D, int BLK, int NP, int S, bool PIPE>
 struct BsaCfg {
@@ -180,7 +176,7 @@ struct BsaCfg {
   static constexpr int JN = KVB / 16 / (QW * 64);  // DMA loads per thread per tile
   // K operand k-steps of the next tile read at the top of a step (the rest
   // are read inside the MFMA / softmax interleave)
-  static constexpr int KPRE = SA_KPRE < D / 16 ? SA_KPRE : D / 16;
+  static constexpr int KPRE = kKPre < D / 16 ? kKPre : D / 16;
   static constexpr int KPA = KPRE > 0 ? KPRE : 1;
   static_assert(S >= 1 && S <= 3 && (S >= 2 || !PIPE), "1 to 3 ring slots, at least 2 when pipelined");
   static_assert(JN >= 1 && (KVB / 16) % (QW * 64) == 0, "tiles must split evenly over a group");
@@ -544,7 +540,7 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
 #pragma unroll
         for (int x = 0; x < 2 * (D / 16); ++x) {
           SA_SCHED_GROUP(0x008, 1);
-          SA_SCHED_GROUP(0x002, SA_VGROUP);
+          SA_SCHED_GROUP(0x002, kVGroup);
         }
       }
       SA_SCHED_GROUP(0x002, 128);
@@ -765,31 +761,12 @@ sa_status launch(Kern kern, const BsaArgs& a, int threads, int lds_bytes, hipStr
 // compiled tile shape.  One slot, not pipelined, for whole rows: 4 % (long rows)
 // to 12 % faster than a two-slot ring on the compression-guided, gzip-guided
 // and long-context masks, from the higher occupancy
-#ifndef SA_CFG_64_64
-#define SA_CFG_64_64 1, 1, false
-#endif
-#ifndef SA_CFG_64_128
-#define SA_CFG_64_128 1, 1, false
-#endif
-#ifndef SA_CFG_128_64
-#define SA_CFG_128_64 1, 1, false
-#endif
-#ifndef SA_CFG_128_128
-#define SA_CFG_128_128 1, 1, false
-#endif
-// ... and with each row split over two wave groups (row_split = 2)
-#ifndef SA_CFG2_64_64
-#define SA_CFG2_64_64 2, 2, true
-#endif
-#ifndef SA_CFG2_64_128
-#define SA_CFG2_64_128 2, 2, true
-#endif
-#ifndef SA_CFG2_128_64
-#define SA_CFG2_128_64 2, 2, false
-#endif
-#ifndef SA_CFG2_128_128
-#define SA_CFG2_128_128 2, 2, false
-#endif
+#define SA_CFG_WHOLE 1, 1, false
+// ... and with each row split over two wave groups (row_split = 2): a two-slot
+// ring, software-pipelined at d = 64 (at d = 128 the pipelined form needs more
+// than 256 registers)
+#define SA_CFG_SPLIT64 2, 2, true
+#define SA_CFG_SPLIT128 2, 2, false
 
 // The kernel must be named in a non-template context for its host stub to be
 // emitted, hence a macro rather than a function template.
@@ -900,16 +877,16 @@ sa_status fwd_setup(int32_t dtype, const void* q, const void* k, const void* v, 
 sa_status fwd_launch(const BsaArgs& a, int32_t dtype, int32_t d, int32_t block, int32_t row_split,
                      hipStream_t stream) {
   if (dtype == SA_BF16 && row_split == 2) {
-    if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG2_64_64, "bsa_fwd_bf16<64,64,split>");
-    if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG2_64_128, "bsa_fwd_bf16<64,128,split>");
-    if (d == 128 && block == 64) SA_LAUNCH_BF16(128, 64, SA_CFG2_128_64, "bsa_fwd_bf16<128,64,split>");
-    SA_LAUNCH_BF16(128, 128, SA_CFG2_128_128, "bsa_fwd_bf16<128,128,split>");
+    if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG_SPLIT64, "bsa_fwd_bf16<64,64,split>");
+    if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG_SPLIT64, "bsa_fwd_bf16<64,128,split>");
+    if (d == 128 && block == 64) SA_LAUNCH_BF16(128, 64, SA_CFG_SPLIT128, "bsa_fwd_bf16<128,64,split>");
+    SA_LAUNCH_BF16(128, 128, SA_CFG_SPLIT128, "bsa_fwd_bf16<128,128,split>");
   }
   if (dtype == SA_BF16) {
-    if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG_64_64, "bsa_fwd_bf16<64,64>");
-    if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG_64_128, "bsa_fwd_bf16<64,128>");
-    if (d == 128 && block == 64) SA_LAUNCH_BF16(128, 64, SA_CFG_128_64, "bsa_fwd_bf16<128,64>");
-    SA_LAUNCH_BF16(128, 128, SA_CFG_128_128, "bsa_fwd_bf16<128,128>");
+    if (d == 64 && block == 64) SA_LAUNCH_BF16(64, 64, SA_CFG_WHOLE, "bsa_fwd_bf16<64,64>");
+    if (d == 64 && block == 128) SA_LAUNCH_BF16(64, 128, SA_CFG_WHOLE, "bsa_fwd_bf16<64,128>");
+    if (d == 128 && block == 64) SA_LAUNCH_BF16(128, 64, SA_CFG_WHOLE, "bsa_fwd_bf16<128,64>");
+    SA_LAUNCH_BF16(128, 128, SA_CFG_WHOLE, "bsa_fwd_bf16<128,128>");
   }
   if (d == 64 && block == 64) return launch(bsa_fwd_f32_kernel<64, 64>, a, 64, 0, stream, "bsa_fwd_f32<64,64>");
   if (d == 64 && block == 128) return launch(bsa_fwd_f32_kernel<64, 128>, a, 128, 0, stream, "bsa_fwd_f32<64,128>");

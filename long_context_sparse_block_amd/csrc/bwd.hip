@@ -444,30 +444,18 @@ __device__ __forceinline__ sa::u32x4 pack8(const float* x) {
 // tile runs a variant of its own and the others skip the mask; with ILV both
 // halves sit in one basic block so that their MFMAs and VALU work interleave
 // (more registers).
-#ifndef SA_BWD_SPLIT64
-#define SA_BWD_SPLIT64 1
-#endif
-#ifndef SA_BWD_SPLIT128
-#define SA_BWD_SPLIT128 0
-#endif
-#ifndef SA_BWD_ILV64
-#define SA_BWD_ILV64 0
-#endif
-#ifndef SA_BWD_ILV128
-#define SA_BWD_ILV128 0
-#endif
+// d = 64: the diagonal tile has a variant of its own; d = 128: one masked
+// variant (two would keep twice the operand addresses live).
+template <int D>
+struct TileCfg {
+  static constexpr bool SPLIT = D == 64;
+};
 template <int D, typename F>
 __device__ __forceinline__ void bwd_tile(bool diag, F& half) {
-  constexpr bool SPLIT = D == 64 ? SA_BWD_SPLIT64 : SA_BWD_SPLIT128;
-  constexpr bool ILV = D == 64 ? SA_BWD_ILV64 : SA_BWD_ILV128;
+  constexpr bool SPLIT = TileCfg<D>::SPLIT;
   auto run = [&](auto mask_tag) {
-    if constexpr (ILV) {
-      half(0, mask_tag);
-      half(1, mask_tag);
-    } else {
 #pragma unroll 1
-      for (int x = 0; x < 2; ++x) half(x, mask_tag);
-    }
+    for (int x = 0; x < 2; ++x) half(x, mask_tag);
   };
   if constexpr (SPLIT) {
     if (diag)
@@ -1195,9 +1183,7 @@ sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t s
 
 // 64-row tiles per dK/dV work item: longer columns are split over several
 // workgroups (an item's list of at most 64 entries is held in VGPR lanes)
-#ifndef SA_BWD_CHUNK_TILES
-#define SA_BWD_CHUNK_TILES 64
-#endif
+constexpr int kChunkTiles = 64;
 
 
 template <int D, int BLK>
@@ -1297,7 +1283,7 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
   a.stat = (sa::f32x2*)(ws + wsl.stat);
   a.pre = (int32_t*)(ws + wsl.pre);
   a.acc = (float*)(ws + wsl.acc);
-  a.chunk = std::max(1, std::min(64, SA_BWD_CHUNK_TILES / std::max(1, block / 64)));  // CSR entries per item
+  a.chunk = std::max(1, std::min(64, kChunkTiles / std::max(1, block / 64)));  // CSR entries per item
   if (block < 1 || causal < 0 || causal > 1 || col_capacity < 0 || row_capacity < 0) return SA_ERR_INVALID;
   if (num_groups < 1 || mask_batch_stride < 0 || mask_head_stride < 0) return SA_ERR_INVALID;
   if ((int64_t)(B - 1) * mask_batch_stride + (int64_t)(H - 1) * mask_head_stride >= num_groups)

@@ -135,15 +135,12 @@ __device__ __forceinline__ int swz(int c, int row) {
   return c ^ ((r & 1) | ((r & 2) << 1) | ((r & 4) >> 1));
 }
 
-#ifndef SA_OFF_FC64
-#define SA_OFF_FC64 2
-#endif
-#ifndef SA_OFF_TPW_DIV
-#define SA_OFF_TPW_DIV 4
-#endif
-#ifndef SA_OFF_WAVES64
-#define SA_OFF_WAVES64 3
-#endif
+// far rungs per register batch; resident workgroups per CU at d = 64; tiles
+// per workgroup aim at this many workgroups per resident slot of the chip
+// (each measured best against its neighbours)
+constexpr int kFarBatch = 2;
+constexpr int kWaves64 = 3;
+constexpr int kTilesDiv = 4;
 
 template <int D, int NS>
 struct MCfg {
@@ -158,11 +155,11 @@ struct MCfg {
   static constexpr int CPR = D / 8;          // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;    // rows per copy wave-instruction
   static constexpr int IPW = ROWB / 64;      // copy wave-instructions per wave, block and matrix
-  static constexpr int FC = D == 64 ? SA_OFF_FC64 : 2;  // far rungs per register batch (even)
+  static constexpr int FC = kFarBatch;  // far rungs per register batch (even)
 };
 
 template <int D, int NS>
-__global__ __launch_bounds__(256, D == 64 ? SA_OFF_WAVES64 : 2) void offset_mfma_kernel(OffArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? kWaves64 : 2) void offset_mfma_kernel(OffArgs a) {
   using C = MCfg<D, NS>;
   constexpr int NC = C::NC, NDT = C::NDT, FC = C::FC, ROWB = C::ROWB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -758,10 +755,7 @@ static sa_status offset_run(int32_t dtype, const void* q, const void* k, const v
     // (256 CUs x 3 resident workgroups); a longer walk re-copies fewer halo rows
     const int64_t ntiles = ((int64_t)N + 63) / 64;
     const int64_t total = (int64_t)B * H * ntiles;
-    a.tpw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ntiles, total / (SA_OFF_TPW_DIV * 256 * 3)));
-#ifdef SA_OFF_TPW_FORCE
-    a.tpw = (int32_t)std::min<int64_t>(ntiles, SA_OFF_TPW_FORCE);
-#endif
+    a.tpw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(ntiles, total / (kTilesDiv * 256 * 3)));
     a.nchunk = (int32_t)((ntiles + a.tpw - 1) / a.tpw);
     if ((int64_t)B * H * a.nchunk > 0x7fffffffll) return SA_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((int64_t)B * H * a.nchunk));
