@@ -2,15 +2,15 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
-The pages draw random blocks (BigBird, Sec. 2: "r independently and uniformly
-sampled key indices"; Sec. 3 sketch: a random permutation prefix per row) and
-the synthetic workloads draw Bernoulli literal flags.  Neither page fixes a
+The pages draw random blocks (BigBird, Sec. 2: r key indices per query, drawn
+uniformly and independently; Sec. 3 sketch: a prefix of a random permutation
+per row) and the synthetic workloads draw Bernoulli literal flags.  Neither page fixes a
 generator, so both sides of the parity check implement the same published
 counter-based generator, SplitMix64 (G. L. Steele, D. Lea, C. H. Flood, "Fast
 Splittable Pseudorandom Number Generators", OOPSLA 2014), independently, and
 derive every draw from a key that names what is drawn.  The key chain, the
 Bernoulli threshold and the multiply-shift range reduction are this library's
-convention (stated in the design doc), not the pages'.
+convention, written out in the functions below, not the pages'.
 
 All arithmetic is on Python integers reduced modulo 2**64.
 """
