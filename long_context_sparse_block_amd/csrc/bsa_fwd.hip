@@ -24,6 +24,10 @@
 //     the accumulator to the operand registers with one bf16 pack and no LDS
 //     round trip.  The V^T operand comes from row-major V in LDS through
 //     transpose reads (ds_read_b64_tr_b16);
+//   * in the one-slot kernels the K and V^T operand reads of a step are issued
+//     in a fixed order a few MFMAs ahead of their use (scheduling barriers
+//     hold that order; the compiler's own waits count them), instead of each
+//     MFMA waiting out a full LDS round trip;
 //   * 16-byte LDS chunks are XOR-swizzled so that the K operand reads
 //     (ds_read_b128, sa::lds_slot) and the V^T transpose reads
 //     (sa::lds_slot_tr) are free of bank conflicts on gfx950's 64-bank LDS;
@@ -160,6 +164,11 @@ __device__ __forceinline__ void wait_vm_units(int c) {
 // scheduled after each S(n+1) MFMA.
 constexpr int kKPre = 4;
 constexpr int kVGroup = 12;
+// One-slot kernels: MFMA operands read from LDS this many MFMAs ahead (K side),
+// and V operands put in flight before the softmax of a tile.
+constexpr int kKAhead = 4;
+constexpr int kVAhead = 2;
+constexpr int kVRing = 4;
 
 template <int D, int BLK, int NP, int S, bool PIPE>
 struct BsaCfg {
@@ -283,6 +292,25 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
   const uint32_t vring = kring + C::VRING;
   const uint8_t* const kring_p = smem + grp * C::KVB;
   const uint8_t* const vring_p = kring_p + C::VRING;
+  // One-slot kernels read the MFMA operands in a fixed order, a few MFMAs
+  // ahead of their use.  K operand of k-step k for the lane's key lq (keys
+  // 32 kt + lq sit 32 rows further, the same slot pattern); V^T operand of the
+  // lane's d-column group dt for keys 4 hl + (lane & 15) / 4 (16 u + 8 more
+  // rows down share the pattern, period 4).
+  constexpr bool kHand = !PIPE && S == 1;
+  const uint8_t* kop_p[D / 16];
+  const uint8_t* vop_p[D / 32];
+  if constexpr (kHand) {
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) kop_p[k] = kring_p + lq * C::ROWB + 16 * sa::lds_slot<D>(2 * k + hl, lq);
+    const int gi = lane >> 4, ii = lane & 15;
+    const int key0 = 4 * hl + (ii >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + 16 * (gi & 1) + 4 * (ii & 3);
+      vop_p[dt] = vring_p + key0 * C::ROWB + 16 * sa::lds_slot_tr<D>(col >> 3, key0) + 8 * ((col >> 2) & 1);
+    }
+  }
 
   // Copies of one 64-key tile (key block kb >= 0, sub-tile sub) into a ring
   // slot.  Byte offsets of a block are below 2^32 (the host bounds the
@@ -342,6 +370,26 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
       return *(const sa::u32x4*)(ks + key * C::ROWB + sa::lds_slot<D>(2 * k + hl, key) * 16);
     };
 
+    // S^T = K Q^T of the one slot, operand m = 2 k + kt read kKAhead MFMAs
+    // before its use (sched barriers keep that order; the compiler counts the
+    // reads when it places the waits).
+    auto qk_hand = [&](sa::f32x16(&dst)[2]) {
+      constexpr int NS = 2 * (D / 16);
+      constexpr int R = kKAhead < NS ? kKAhead : NS;
+      sa::u32x4 buf[NS];
+      auto rd = [&](auto m) {
+        constexpr int M = decltype(m)::value;
+        buf[M] = *(const sa::u32x4*)(kop_p[M >> 1] + (M & 1) * 32 * C::ROWB);
+      };
+      sa::static_for<0, R>(rd);
+      sa::static_for<0, NS>([&](auto m) {
+        constexpr int M = decltype(m)::value;
+        SA_SCHED_BARRIER();
+        dst[M & 1] = M < 2 ? sa::mfma32_z(buf[M], qr[M >> 1]) : sa::mfma32(buf[M], qr[M >> 1], dst[M & 1]);
+        if constexpr (M + R < NS) rd(std::integral_constant<int, M + R>{});
+      });
+      SA_SCHED_BARRIER();
+    };
     auto qk = [&](const uint8_t* ks, sa::f32x16(&dst)[2]) {
 #pragma unroll
       for (int k = 0; k < D / 16; ++k)
@@ -388,6 +436,16 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
       const int pn = S == 2 && PAR >= 0 ? PAR : n % S;
       SA_SCHED_BARRIER();  // the previous step's MFMAs are issued before this wait
       int32_t qn = -1;  // key block of the newest tile put in flight
+      // V^T operands of the one-slot kernels, j = u (D / 32) + dt: keys
+      // 16 u .. 16 u + 15, d-columns 32 dt .. 32 dt + 31
+      constexpr int NV = 4 * (D / 32);
+      sa::u32x4 vbuf[NV];
+      auto vread = [&](auto j) {
+        constexpr int J = decltype(j)::value, U = J / (D / 32), DT = J % (D / 32);
+        const sa::u32x2 lo = sa::lds_read_tr16(vop_p[DT] + U * 16 * C::ROWB);
+        const sa::u32x2 hi = sa::lds_read_tr16(vop_p[DT] + U * 16 * C::ROWB + 8 * C::ROWB);
+        vbuf[J] = sa::u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
       if constexpr (PIPE) {
         // K(n+1) and V(n) must have landed (all waves): wait for the copies
         // issued up to step n+1-S; the barrier then also frees K(n), V(n-1).
@@ -405,7 +463,8 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
         // K(n) and V(n) must have landed (copied at the end of step n-1)
         wait_vmcnt<0>();
         ring_barrier();
-        qk(kring_p, cur);
+        qk_hand(cur);
+        sa::static_for<0, kVAhead>(vread);  // in flight during the softmax
       } else {
         // K(n) and V(n) must have landed; the barrier also frees tile n-1
         if (S == 3)
@@ -512,6 +571,32 @@ void bsa_fwd_bf16_kernel(BsaArgs a) {
             pb[2 * kt + h2][w] = sa::pack_bf16x2(sa::fast_exp2(__builtin_fmaf(cur[kt][e], c2, -m_used)),
                                                  sa::fast_exp2(__builtin_fmaf(cur[kt][e + 1], c2, -m_used)));
           }
+      if constexpr (kHand) {
+        // O^T += V^T P^T, operands read kVRing MFMAs ahead; then the row sums
+        // over the rounded P actually fed to the MFMA, on the VALU while the
+        // last MFMAs run
+        sa::static_for<kVAhead, kVRing>(vread);
+        sa::static_for<0, NV>([&](auto j) {
+          constexpr int J = decltype(j)::value;
+          SA_SCHED_BARRIER();
+          oacc[J % (D / 32)] = sa::mfma32(vbuf[J], pb[J / (D / 32)], oacc[J % (D / 32)]);
+          if constexpr (J + kVRing < NV) vread(std::integral_constant<int, J + kVRing>{});
+        });
+        SA_SCHED_BARRIER();
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) ls[0] = sa::dot2_bf16(pb[u][w], 0x3f803f80u, ls[0]);
+        if (n + 1 < NI) {
+          // every wave has read tile n (its LDS reads returned): refill the slots
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          ring_barrier();
+          q0 = tile_kb(n + 1);
+          dma_k(n + 1, q0, 0);
+          dma_v(n + 1, q0, 0);
+        }
+        return;
+      }
       // row sums over the rounded P actually fed to the MFMA
 #pragma unroll
       for (int u = 0; u < 4; ++u)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -316,6 +318,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
   typedef __attribute__((ext_vector_type(4))) short s16x4;
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds);
   return __builtin_bit_cast(u32x2, v);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 in order, so that
+// every index is a compile-time constant (unrolled at the source level).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 }  // namespace sa
