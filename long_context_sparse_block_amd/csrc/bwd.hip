@@ -559,13 +559,36 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
       // one 32-key half; MASK: apply the causal triangle when diag
       auto half = [&](int kt, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        // S^T and dP^T [32 keys x 32 queries]
+        // S^T and dP^T [32 keys x 32 queries]: operand m = 2u (K rows) or
+        // 2u + 1 (V rows), read RA MFMAs ahead of its use (scheduling
+        // barriers hold the order; the compiler counts the reads in its waits)
+        constexpr int NA = 2 * NU, RA = 4;
+        sa::u32x4 abuf[NA];
+        auto ard = [&](auto m) {
+          constexpr int Mi = decltype(m)::value;
+          if constexpr (Mi < NA) abuf[Mi] = L::rows_a((Mi & 1) ? vs : ks, 32 * kt, Mi >> 1, lane);
+        };
+        sa::static_for<0, RA>(ard);
         sa::f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          s = sa::mfma32(L::rows_a(ks, 32 * kt, u, lane), qb[u], s);
-          dp = sa::mfma32(L::rows_a(vs, 32 * kt, u, lane), gb[u], dp);
-        }
+        sa::static_for<0, NA>([&](auto m) {
+          constexpr int Mi = decltype(m)::value;
+          SA_SCHED_BARRIER();
+          if constexpr (Mi & 1)
+            dp = sa::mfma32(abuf[Mi], gb[Mi >> 1], dp);
+          else
+            s = sa::mfma32(abuf[Mi], qb[Mi >> 1], s);
+          ard(std::integral_constant<int, Mi + RA>{});
+        });
+        SA_SCHED_BARRIER();
+        // K^T operands of dQ^T += K^T dS^T, j = st NT + dt, the first RC in
+        // flight during the VALU work below
+        constexpr int NC = 2 * NT, RC = 2;
+        sa::u32x4 cbuf[NC];
+        auto crd = [&](auto jj) {
+          constexpr int J = decltype(jj)::value;
+          if constexpr (J < NC) cbuf[J] = L::rows_tr(ks, 32 * kt, J / NT, J % NT, lane);
+        };
+        sa::static_for<0, RC>(crd);
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -574,13 +597,16 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
           // keys after the query
           if (MASK && diag && ksub + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3) > qoff) ds[r] = 0.f;
         }
+        const sa::u32x4 bo[2] = {pack8(ds), pack8(ds + 8)};
+        crd(std::integral_constant<int, RC>{});  // RC + 1 ahead from here on
         // dQ^T [d x queries] += K^T [d x keys] dS^T [keys x queries]
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const sa::u32x4 bo = pack8(ds + 8 * st);
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::mfma32(L::rows_tr(ks, 32 * kt, st, dt, lane), bo, acc[dt]);
-        }
+        sa::static_for<0, NC>([&](auto jj) {
+          constexpr int J = decltype(jj)::value;
+          SA_SCHED_BARRIER();
+          acc[J % NT] = sa::mfma32(cbuf[J], bo[J / NT], acc[J % NT]);
+          crd(std::integral_constant<int, J + RC + 1>{});
+        });
+        SA_SCHED_BARRIER();
       };
       bwd_tile<D>(diag, half);
     }
@@ -816,18 +842,48 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
           // base keeps the compiler from holding them in registers)
           uint32_t vrows = vblk + (uint32_t)(32 * kg / 64) * M::TB;
           asm volatile("" : "+s"(vrows));
-          // S and dP [32 queries x 32 keys]
+          // S and dP [32 queries x 32 keys]: MFMA m = 2u takes the Q rows,
+          // m = 2u + 1 the dO rows (and, VL, the V rows); their reads are issued
+          // LA MFMAs ahead of use (scheduling barriers hold the order; the
+          // compiler counts the reads in its waits)
+          constexpr int NA = 2 * NU, LA = 2;
+          sa::u32x4 qa[NU], ga[NU], va[VL ? NU : 1];
+          auto ard = [&](auto m) {
+            constexpr int Mi = decltype(m)::value, U = Mi >> 1;
+            if constexpr (Mi < NA && (Mi & 1) == 0) qa[U] = L::rows_a(qs, 32 * qt, U, lane);
+            if constexpr (Mi < NA && (Mi & 1) == 1) {
+              ga[U] = L::rows_a(gs, 32 * qt, U, lane);
+              if constexpr (VL) va[U] = L::rows_a_lds(vrows, (32 * kg) % 64, U, lane);
+            }
+          };
+          sa::static_for<0, LA>(ard);
           sa::f32x16 s = {}, dp = {};
-#pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            s = sa::mfma32(L::rows_a(qs, 32 * qt, u, lane), kb_[u], s);
-            sa::u32x4 vop;
-            if constexpr (VL)
-              vop = L::rows_a_lds(vrows, (32 * kg) % 64, u, lane);
-            else
-              vop = vb_[u];
-            dp = sa::mfma32(L::rows_a(gs, 32 * qt, u, lane), vop, dp);
-          }
+          sa::static_for<0, NA>([&](auto m) {
+            constexpr int Mi = decltype(m)::value, U = Mi >> 1;
+            SA_SCHED_BARRIER();
+            if constexpr (Mi & 1) {
+              if constexpr (VL)
+                dp = sa::mfma32(ga[U], va[U], dp);
+              else
+                dp = sa::mfma32(ga[U], vb_[U], dp);
+            } else {
+              s = sa::mfma32(qa[U], kb_[U], s);
+            }
+            ard(std::integral_constant<int, Mi + LA>{});
+          });
+          SA_SCHED_BARRIER();
+          // transposed A operands of dV^T += dO^T P and dK^T += Q^T dS, j =
+          // st NT + dt; the first in flight during the VALU work below
+          constexpr int NC = 2 * NT;
+          sa::u32x4 gt[NC], qtr[NC];
+          auto crd = [&](auto jj) {
+            constexpr int J = decltype(jj)::value;
+            if constexpr (J < NC) {
+              gt[J] = L::rows_tr(gs, 32 * qt, J / NT, J % NT, lane);
+              qtr[J] = L::rows_tr(qs, 32 * qt, J / NT, J % NT, lane);
+            }
+          };
+          crd(std::integral_constant<int, 0>{});
           float p[16], ds[16];
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -845,15 +901,16 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
             }
           }
           // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const sa::u32x4 pb = pack8(p + 8 * st), sb = pack8(ds + 8 * st);
-#pragma unroll
-            for (int dt = 0; dt < NT; ++dt) {
-              dv[dt] = sa::mfma32(L::rows_tr(gs, 32 * qt, st, dt, lane), pb, dv[dt]);
-              dk[dt] = sa::mfma32(L::rows_tr(qs, 32 * qt, st, dt, lane), sb, dk[dt]);
-            }
-          }
+          const sa::u32x4 pb[2] = {pack8(p), pack8(p + 8)}, sb[2] = {pack8(ds), pack8(ds + 8)};
+          crd(std::integral_constant<int, 1>{});  // two ahead from here on
+          sa::static_for<0, NC>([&](auto jj) {
+            constexpr int J = decltype(jj)::value;
+            SA_SCHED_BARRIER();
+            dv[J % NT] = sa::mfma32(gt[J], pb[J / NT], dv[J % NT]);
+            dk[J % NT] = sa::mfma32(qtr[J], sb[J / NT], dk[J % NT]);
+            crd(std::integral_constant<int, J + 2>{});
+          });
+          SA_SCHED_BARRIER();
         };
         bwd_tile<D>(diag, half);
       }
