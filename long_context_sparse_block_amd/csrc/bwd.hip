@@ -376,6 +376,28 @@ struct TileLds {
     typedef __attribute__((address_space(3))) const sa::u32x4* lptr;
     return *(lptr)(uintptr_t)(t + row * ROWB + bswz<D>(2 * u + (lane >> 5), row) * 16);
   }
+  // The slot pattern depends on a row's low four bits only, so for r0 a
+  // multiple of 16 the reads above and below are a lane-constant byte offset
+  // from t + r0 ROWB: a_off(u) for rows_a, tr_off(dt, ab) for the two reads
+  // of rows_tr (ab = 0: rows 4(l/32) + m, ab = 1: 8 rows further).
+  static __device__ __forceinline__ int a_off(int u, int lane) {
+    const int row = lane & 31;
+    return row * ROWB + bswz<D>(2 * u + (lane >> 5), row) * 16;
+  }
+  static __device__ __forceinline__ int tr_off(int dt, int ab, int lane) {
+    const int grp = lane >> 4, p = lane & 15;
+    const int d0 = 32 * dt + 16 * (grp & 1) + 4 * (p & 3);
+    const int r = 4 * (grp >> 1) + (p >> 2) + 8 * ab;
+    return r * ROWB + bswz<D>(d0 >> 3, r) * 16 + (d0 & 7) * 2;
+  }
+  static __device__ __forceinline__ sa::u32x4 at_a(const uint8_t* base, int off) {
+    return *(const sa::u32x4*)(base + off);
+  }
+  static __device__ __forceinline__ sa::u32x4 at_tr(const uint8_t* base, int offa, int offb) {
+    const sa::u32x2 x = sa::lds_read_tr16(base + offa);
+    const sa::u32x2 y = sa::lds_read_tr16(base + offb);
+    return sa::u32x4{x[0], x[1], y[0], y[1]};
+  }
   // transposed A operand: d rows 32 dt + l%32, k = tile rows 16 s + 8(e/4) + 4(l/32) + e%4
   static __device__ __forceinline__ sa::u32x4 rows_tr(const uint8_t* t, int r0, int s, int dt, int lane) {
     const int grp = lane >> 4, p = lane & 15, h = grp >> 1;
@@ -519,6 +541,11 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
   for (int dt = 0; dt < NT; ++dt) acc[dt] = sa::f32x16{};
   const typename M::Off offK = M::lane_off(w, lane, ks2), offV = M::lane_off(w, lane, vs2);
   const uint32_t ring = sa::lds_addr(smem);
+  int aoff[NU], troff[NT][2];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) aoff[u] = L::a_off(u, lane);
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) troff[dt][0] = L::tr_off(dt, 0, lane), troff[dt][1] = L::tr_off(dt, 1, lane);
   int32_t e0, e1;
   row_range(a, g, i, e0, e1);
   const int32_t limit = a.causal ? i + 1 : a.nb;  // usable key blocks are < limit
@@ -564,17 +591,22 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
         // barriers hold the order; the compiler counts the reads in its waits)
         constexpr int NA = 2 * NU, RA = 4;
         sa::u32x4 abuf[NA];
+        const uint8_t* kh = ks + 32 * kt * L::ROWB;  // the half's 32 K rows (V: M::TB further)
         auto ard = [&](auto m) {
           constexpr int Mi = decltype(m)::value;
-          if constexpr (Mi < NA) abuf[Mi] = L::rows_a((Mi & 1) ? vs : ks, 32 * kt, Mi >> 1, lane);
+          if constexpr (Mi < NA) abuf[Mi] = L::at_a(kh + ((Mi & 1) ? M::TB : 0), aoff[Mi >> 1]);
         };
         sa::static_for<0, RA>(ard);
-        sa::f32x16 s = {}, dp = {};
+        sa::f32x16 s, dp;
         sa::static_for<0, NA>([&](auto m) {
           constexpr int Mi = decltype(m)::value;
           SA_SCHED_BARRIER();
-          if constexpr (Mi & 1)
+          if constexpr (Mi == 1)
+            dp = sa::mfma32_z(abuf[Mi], gb[0]);
+          else if constexpr (Mi & 1)
             dp = sa::mfma32(abuf[Mi], gb[Mi >> 1], dp);
+          else if constexpr (Mi == 0)
+            s = sa::mfma32_z(abuf[Mi], qb[0]);
           else
             s = sa::mfma32(abuf[Mi], qb[Mi >> 1], s);
           ard(std::integral_constant<int, Mi + RA>{});
@@ -586,7 +618,7 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
         sa::u32x4 cbuf[NC];
         auto crd = [&](auto jj) {
           constexpr int J = decltype(jj)::value;
-          if constexpr (J < NC) cbuf[J] = L::rows_tr(ks, 32 * kt, J / NT, J % NT, lane);
+          if constexpr (J < NC) cbuf[J] = L::at_tr(kh + 16 * (J / NT) * L::ROWB, troff[J % NT][0], troff[J % NT][1]);
         };
         sa::static_for<0, RC>(crd);
         float ds[16];
@@ -729,6 +761,11 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
   const uint32_t ring = sa::lds_addr(smem);
   const uint32_t vblk = ring + S * SLOT;  // V rows of the key block (VL)
   const uint32_t soff = 16u * (uint32_t)(lane & 31);  // statistics: 2 rows per lane, lanes 32.. repeat
+  int aoff[NU], troff[NT][2];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) aoff[u] = L::a_off(u, lane);
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) troff[dt][0] = L::tr_off(dt, 0, lane), troff[dt][1] = L::tr_off(dt, 1, lane);
   bool first = true;
   for (int32_t item = blockIdx.x; item < items; item += gridDim.x) {
     int64_t c;
@@ -848,26 +885,29 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
           // compiler counts the reads in its waits)
           constexpr int NA = 2 * NU, LA = 2;
           sa::u32x4 qa[NU], ga[NU], va[VL ? NU : 1];
+          const uint8_t* qh = qs + 32 * qt * L::ROWB;  // the half's 32 Q rows (dO: M::TB further)
           auto ard = [&](auto m) {
             constexpr int Mi = decltype(m)::value, U = Mi >> 1;
-            if constexpr (Mi < NA && (Mi & 1) == 0) qa[U] = L::rows_a(qs, 32 * qt, U, lane);
+            if constexpr (Mi < NA && (Mi & 1) == 0) qa[U] = L::at_a(qh, aoff[U]);
             if constexpr (Mi < NA && (Mi & 1) == 1) {
-              ga[U] = L::rows_a(gs, 32 * qt, U, lane);
+              ga[U] = L::at_a(qh + M::TB, aoff[U]);
               if constexpr (VL) va[U] = L::rows_a_lds(vrows, (32 * kg) % 64, U, lane);
             }
           };
           sa::static_for<0, LA>(ard);
-          sa::f32x16 s = {}, dp = {};
+          sa::f32x16 s, dp;
           sa::static_for<0, NA>([&](auto m) {
             constexpr int Mi = decltype(m)::value, U = Mi >> 1;
             SA_SCHED_BARRIER();
             if constexpr (Mi & 1) {
+              sa::u32x4 vop;
               if constexpr (VL)
-                dp = sa::mfma32(ga[U], va[U], dp);
+                vop = va[U];
               else
-                dp = sa::mfma32(ga[U], vb_[U], dp);
+                vop = vb_[U];
+              dp = Mi == 1 ? sa::mfma32_z(ga[U], vop) : sa::mfma32(ga[U], vop, dp);
             } else {
-              s = sa::mfma32(qa[U], kb_[U], s);
+              s = Mi == 0 ? sa::mfma32_z(qa[U], kb_[U]) : sa::mfma32(qa[U], kb_[U], s);
             }
             ard(std::integral_constant<int, Mi + LA>{});
           });
@@ -879,8 +919,9 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
           auto crd = [&](auto jj) {
             constexpr int J = decltype(jj)::value;
             if constexpr (J < NC) {
-              gt[J] = L::rows_tr(gs, 32 * qt, J / NT, J % NT, lane);
-              qtr[J] = L::rows_tr(qs, 32 * qt, J / NT, J % NT, lane);
+              const uint8_t* qb16 = qh + 16 * (J / NT) * L::ROWB;
+              gt[J] = L::at_tr(qb16 + M::TB, troff[J % NT][0], troff[J % NT][1]);
+              qtr[J] = L::at_tr(qb16, troff[J % NT][0], troff[J % NT][1]);
             }
           };
           crd(std::integral_constant<int, 0>{});
