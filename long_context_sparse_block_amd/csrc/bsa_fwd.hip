@@ -164,11 +164,12 @@ __device__ __forceinline__ void wait_vm_units(int c) {
 // scheduled after each S(n+1) MFMA.
 constexpr int kKPre = 4;
 constexpr int kVGroup = 12;
-// One-slot kernels: MFMA operands read from LDS this many MFMAs ahead (K side),
-// and V operands put in flight before the softmax of a tile.
-constexpr int kKAhead = 4;
+// One-slot kernels: K operands read this many MFMAs ahead of their use, V
+// operands put in flight before the softmax of a tile and this many ahead
+// during O += V P (deeper rings spill at d = 128).
+constexpr int kKAhead = 3;
 constexpr int kVAhead = 2;
-constexpr int kVRing = 4;
+constexpr int kVRing = 3;
 
 template <int D, int BLK, int NP, int S, bool PIPE>
 struct BsaCfg {
