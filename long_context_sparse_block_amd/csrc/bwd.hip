@@ -834,15 +834,20 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
     for (int t = 0; t < NT; ++t) dk[t] = sa::f32x16{}, dv[t] = sa::f32x16{};
     const int T = cnt * SUBS;
     auto issue = [&](int m) {
-      const int32_t qb = sa::readlane(lq, m / SUBS), h = sa::readlane(lh, m / SUBS);
+      // without grouped query heads every entry's head is the K/V head
+      const int32_t qb = sa::readlane(lq, m / SUBS), h = rep == 1 ? kvh : sa::readlane(lh, m / SUBS);
       const int64_t r0 = (int64_t)(qb < 0 ? j : qb) * BLK + 64 * (m % SUBS);
       const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
       const uint16_t* G = (const uint16_t*)a.dout + b * a.st[TDO][0] + h * a.st[TDO][1];
       const float* st = (const float*)(a.stat + ((int64_t)b * a.H + h) * a.N + r0);
       const uint32_t dst = ring + (m % S) * SLOT;
-      M::copy(Q + r0 * a.st[TQ][2], a.st[TQ][2], M::lane_off(w, lane, a.st[TQ][2]), dst, w);
-      M::copy(G + r0 * a.st[TDO][2], a.st[TDO][2], M::lane_off(w, lane, a.st[TDO][2]), dst + M::TB, w);
-      if (w == 0) sa::dma16(st, soff, dst + 2 * M::TB);
+      // the per-lane source offsets are recomputed here (a few VALU
+      // instructions) from a fresh lane id: hoisted out of the tile loop they
+      // were spilled, and every copy waited for their reload
+      const int ln = sa::fresh_lane();
+      M::copy(Q + r0 * a.st[TQ][2], a.st[TQ][2], M::lane_off(w, ln, a.st[TQ][2]), dst, w);
+      M::copy(G + r0 * a.st[TDO][2], a.st[TDO][2], M::lane_off(w, ln, a.st[TDO][2]), dst + M::TB, w);
+      if (w == 0) sa::dma16(st, 16u * (uint32_t)(ln & 31), dst + 2 * M::TB);
     };
     if constexpr (VL) {
       // the key block's V rows, 64-row tiles one after the other

@@ -107,6 +107,17 @@ __host__ __device__ inline int32_t draw_distinct(uint64_t seed, uint64_t g, uint
 
 __device__ __forceinline__ int wave_lane() { return __lane_id(); }
 
+// The lane id computed afresh where it is used (v_mbcnt in volatile asm): the
+// compiler can neither merge it with an earlier copy nor hoist it, so it never
+// holds a register across a loop (or spills one) for it.
+__device__ __forceinline__ int fresh_lane() {
+  int l = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+#endif
+  return l;
+}
+
 // Target builtins are wrapped in plain (non-template) device functions: a
 // kernel template that names them directly is not instantiated by the host
 // pass, and its launch stub would be missing.
