@@ -986,16 +986,40 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
               sa::u32x2{sa::pack_bf16x2(y[r], y[r + 1]), sa::pack_bf16x2(y[r + 2], y[r + 3])};
         }
     } else {
+      // A chunk of a split column adds its fp32 partials into the workspace.
+      // They go through LDS (free once the tile loop is done), dK then dV, so
+      // that each atomic instruction covers 64 consecutive floats of one key
+      // row (two cache lines) rather than one float in each of 32 rows; the
+      // 16-byte chunks of a staged row are XOR-swizzled by the key's low four
+      // bits, which keeps the writes of 16 keys at one chunk conflict-free.
+      static_assert(S * SLOT + (VL ? BLK * 2 * D : 0) >= BLK * D * 4, "staging area");
       const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
-      float* pk = a.acc + ((int64_t)bk * a.N + sk) * D;
+      float* const pk = a.acc + ((int64_t)bk * a.N + (int64_t)j * BLK) * D;
+      float* const stage = (float*)smem;
+      const int kl = 32 * kg + (lane & 31);  // this lane's key in the block
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      ring_barrier();  // every wave is done with the ring and the V rows
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
+      for (int mtx = 0; mtx < 2; ++mtx) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int x = 32 * dt + 8 * (r >> 2) + 4 * hl + (r & 3);
-          atomicAdd(pk + x, dk[dt][r]);
-          atomicAdd(pk + plane + x, dv[dt][r]);
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const sa::f32x16& x = mtx == 0 ? dk[dt] : dv[dt];
+            const int c = 8 * dt + 2 * r4 + hl;  // 16-byte chunk of d 32 dt + 8 r4 + 4 hl .. + 3
+            *(sa::f32x4*)(stage + kl * D + 4 * (c ^ (kl & 15))) =
+                sa::f32x4{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
+          }
+        __syncthreads();
+        float* const dst = pk + (mtx == 0 ? 0 : plane);
+#pragma unroll 4
+        for (int i = 0; i < D / 2; ++i) {
+          const int e = tid + i * 2 * BLK;  // element (key e / D, d e % D) of the block
+          const int k = e / D, d = e % D;
+          atomicAdd(dst + e, stage[k * D + 4 * ((d >> 2) ^ (k & 15)) + (d & 3)]);
         }
+        __syncthreads();  // the staging area is reused for dV
+      }
     }
   }
 }
