@@ -1308,9 +1308,11 @@ sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t s
                  : launch(delta_kernel<128, false>, a, blocks, 256, 0, stream, "delta_kernel");
 }
 
-// 64-row tiles per dK/dV work item: longer columns are split over several
-// workgroups (an item's list of at most 64 entries is held in VGPR lanes)
-constexpr int kChunkTiles = 64;
+// CSR entries per dK/dV work item: longer columns are split over several
+// workgroups (an item's list, at most 64 entries, is held in VGPR lanes).
+// 16 measured best at block 64 and 128 (8, 32 and 64 were slower on one of
+// the two block sizes or both).
+constexpr int kChunkEntries = 16;
 
 
 template <int D, int BLK>
@@ -1410,7 +1412,7 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
   a.stat = (sa::f32x2*)(ws + wsl.stat);
   a.pre = (int32_t*)(ws + wsl.pre);
   a.acc = (float*)(ws + wsl.acc);
-  a.chunk = std::max(1, std::min(64, kChunkTiles / std::max(1, block / 64)));  // CSR entries per item
+  a.chunk = kChunkEntries;  // CSR entries per item
   if (block < 1 || causal < 0 || causal > 1 || col_capacity < 0 || row_capacity < 0) return SA_ERR_INVALID;
   if (num_groups < 1 || mask_batch_stride < 0 || mask_head_stride < 0) return SA_ERR_INVALID;
   if ((int64_t)(B - 1) * mask_batch_stride + (int64_t)(H - 1) * mask_head_stride >= num_groups)
