@@ -323,7 +323,7 @@ def test_bsa_bwd_long_context_full_size_sampled_heads():
     """The long-context workload at full size ([1, 16, 65536, 128], block 128),
     run as the bench runs it; whole heads 0 and 15 checked against the oracle.
     19 of its 512 rows list 65 to 83 key blocks (a second dQ pass) and the four
-    global key blocks are listed by every later query block (16 dK / dV work
+    global key blocks are listed by every later query block (32 dK / dV work
     items each)."""
     require_gpu()
     w = wl.BLOCK_WORKLOADS["long-context"]
