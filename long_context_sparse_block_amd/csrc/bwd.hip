@@ -626,8 +626,14 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const float p = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -l2));
           ds[r] = p * (dp[r] - dd);
-          // keys after the query
-          if (MASK && diag && ksub + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3) > qoff) ds[r] = 0.f;
+        }
+        if (MASK && diag) {
+          // keys after the query (diagonal tile only: a wave-uniform branch,
+          // kept as one by the volatile asm, so other tiles skip the selects)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (ksub + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3) > qoff) ds[r] = 0.f;
         }
         const sa::u32x4 bo[2] = {pack8(ds), pack8(ds + 8)};
         crd(std::integral_constant<int, RC>{});  // RC + 1 ahead from here on
@@ -941,10 +947,16 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
             for (int cc = 0; cc < 4; ++cc) {
               const int r = 4 * r4 + cc;
               p[r] = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -lv[cc]));
-              // keys after the query
-              if (MASK && diag && koff > qsub + q4 + cc) p[r] = 0.f;
               ds[r] = p[r] * (dp[r] - dv4[cc]);
             }
+          }
+          if (MASK && diag) {
+            // keys after the query (diagonal tile only: a wave-uniform branch,
+            // kept as one by the volatile asm, so other tiles skip the selects)
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (koff > qsub + 32 * qt + 8 * (r >> 2) + 4 * hl + (r & 3)) p[r] = 0.f, ds[r] = 0.f;
           }
           // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
           const sa::u32x4 pb[2] = {pack8(p), pack8(p + 8)}, sb[2] = {pack8(ds), pack8(ds + 8)};
