@@ -631,9 +631,13 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
           // keys after the query (diagonal tile only: a wave-uniform branch,
           // kept as one by the volatile asm, so other tiles skip the selects)
           asm volatile("" ::: "memory");
+          // this lane's query less the key offset 4 hl, from a fresh lane id
+          // (no register is held across the tile loop for it)
+          const int fl = sa::fresh_lane();
+          const int qd = 32 * w + (fl & 31) - 4 * (fl >> 5) - ksub - 32 * kt;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (ksub + 32 * kt + 8 * (r >> 2) + 4 * hl + (r & 3) > qoff) ds[r] = 0.f;
+            if (8 * (r >> 2) + (r & 3) > qd) ds[r] = 0.f;
         }
         const sa::u32x4 bo[2] = {pack8(ds), pack8(ds + 8)};
         crd(std::integral_constant<int, RC>{});  // RC + 1 ahead from here on
@@ -954,9 +958,13 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
             // keys after the query (diagonal tile only: a wave-uniform branch,
             // kept as one by the volatile asm, so other tiles skip the selects)
             asm volatile("" ::: "memory");
+            // this lane's key less its row offset 4 hl, from a fresh lane id
+            // (no register is held across the tile loop for it)
+            const int fl = sa::fresh_lane();
+            const int kd = 32 * kg + (fl & 31) - 4 * (fl >> 5) - qsub - 32 * qt;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (koff > qsub + 32 * qt + 8 * (r >> 2) + 4 * hl + (r & 3)) p[r] = 0.f, ds[r] = 0.f;
+              if (kd > 8 * (r >> 2) + (r & 3)) p[r] = 0.f, ds[r] = 0.f;
           }
           // dV^T += dO^T P,  dK^T += Q^T dS   ([d x queries] x [queries x keys])
           const sa::u32x4 pb[2] = {pack8(p), pack8(p + 8)}, sb[2] = {pack8(ds), pack8(ds + 8)};
