@@ -583,74 +583,116 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
       const uint8_t* vs = ks + M::TB;
       const int ksub = 64 * (n % SUBS);
       const bool diag = a.causal && kb == i;
-      // one 32-key half; MASK: apply the causal triangle when diag
-      auto half = [&](int kt, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        // S^T and dP^T [32 keys x 32 queries]: operand m = 2u (K rows) or
-        // 2u + 1 (V rows), read RA MFMAs ahead of its use (scheduling
-        // barriers hold the order; the compiler counts the reads in its waits)
-        constexpr int NA = 2 * NU, RA = 4;
-        sa::u32x4 abuf[NA];
-        const uint8_t* kh = ks + 32 * kt * L::ROWB;  // the half's 32 K rows (V: M::TB further)
-        auto ard = [&](auto m) {
-          constexpr int Mi = decltype(m)::value;
-          if constexpr (Mi < NA) abuf[Mi] = L::at_a(kh + ((Mi & 1) ? M::TB : 0), aoff[Mi >> 1]);
-        };
-        sa::static_for<0, RA>(ard);
-        sa::f32x16 s, dp;
-        sa::static_for<0, NA>([&](auto m) {
-          constexpr int Mi = decltype(m)::value;
-          SA_SCHED_BARRIER();
-          if constexpr (Mi == 1)
-            dp = sa::mfma32_z(abuf[Mi], gb[0]);
-          else if constexpr (Mi & 1)
-            dp = sa::mfma32(abuf[Mi], gb[Mi >> 1], dp);
-          else if constexpr (Mi == 0)
-            s = sa::mfma32_z(abuf[Mi], qb[0]);
-          else
-            s = sa::mfma32(abuf[Mi], qb[Mi >> 1], s);
-          ard(std::integral_constant<int, Mi + RA>{});
-        });
-        SA_SCHED_BARRIER();
-        // K^T operands of dQ^T += K^T dS^T, j = st NT + dt, the first RC in
-        // flight during the VALU work below
-        constexpr int NC = 2 * NT, RC = 2;
-        sa::u32x4 cbuf[NC];
-        auto crd = [&](auto jj) {
-          constexpr int J = decltype(jj)::value;
-          if constexpr (J < NC) cbuf[J] = L::at_tr(kh + 16 * (J / NT) * L::ROWB, troff[J % NT][0], troff[J % NT][1]);
-        };
-        sa::static_for<0, RC>(crd);
-        float ds[16];
+      // The tile's two 32-key halves, software-pipelined inside the wave: the
+      // S^T / dP^T MFMAs of half 1 run while the VALU turns half 0's S^T and
+      // dP^T into dS^T, and dQ^T += K^T dS^T of half 0 runs while the VALU
+      // works on half 1.  Operand reads go ahead of their MFMAs (scheduling
+      // barriers and group patterns hold the order; the compiler counts the
+      // reads in its waits).  The causal mask of the diagonal tile is applied
+      // in a wave-uniform branch between the phases.
+      constexpr int NA = 2 * NU;  // S^T and dP^T MFMAs of a half: m = 2u (K rows), 2u + 1 (V rows)
+      constexpr int NC = 2 * NT;  // dQ^T MFMAs of a half: j = st NT + dt
+      constexpr int RA = 3, RC = 2;
+      sa::u32x4 abuf[2][NA], cbuf[2][NC];
+      auto ard = [&](auto kt_, auto m) {
+        constexpr int KT = decltype(kt_)::value, Mi = decltype(m)::value;
+        if constexpr (Mi < NA)
+          abuf[KT][Mi] = L::at_a(ks + 32 * KT * L::ROWB + ((Mi & 1) ? M::TB : 0), aoff[Mi >> 1]);
+      };
+      auto crd = [&](auto kt_, auto jj) {
+        constexpr int KT = decltype(kt_)::value, J = decltype(jj)::value;
+        if constexpr (J < NC)
+          cbuf[KT][J] = L::at_tr(ks + (32 * KT + 16 * (J / NT)) * L::ROWB, troff[J % NT][0], troff[J % NT][1]);
+      };
+      using H0 = std::integral_constant<int, 0>;
+      using H1 = std::integral_constant<int, 1>;
+      auto sdp_mfma = [&](auto kt_, auto m, sa::f32x16& s_, sa::f32x16& dp_) {
+        constexpr int KT = decltype(kt_)::value, Mi = decltype(m)::value;
+        if constexpr (Mi == 1)
+          dp_ = sa::mfma32_z(abuf[KT][Mi], gb[0]);
+        else if constexpr (Mi & 1)
+          dp_ = sa::mfma32(abuf[KT][Mi], gb[Mi >> 1], dp_);
+        else if constexpr (Mi == 0)
+          s_ = sa::mfma32_z(abuf[KT][Mi], qb[0]);
+        else
+          s_ = sa::mfma32(abuf[KT][Mi], qb[Mi >> 1], s_);
+      };
+      // dS^T of a half (unmasked)
+      auto dsoft = [&](const sa::f32x16& s_, const sa::f32x16& dp_, float (&ds)[16]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = sa::fast_exp2(__builtin_fmaf(s[r], a.c2, -l2));
-          ds[r] = p * (dp[r] - dd);
-        }
-        if (MASK && diag) {
-          // keys after the query (diagonal tile only: a wave-uniform branch,
-          // kept as one by the volatile asm, so other tiles skip the selects)
+        for (int r = 0; r < 16; ++r) ds[r] = sa::fast_exp2(__builtin_fmaf(s_[r], a.c2, -l2)) * (dp_[r] - dd);
+      };
+      // keys after the query, on the diagonal tile only (a wave-uniform
+      // branch, kept as one by the volatile asm); the lane's query less the
+      // key offset 4 hl comes from a fresh lane id
+      auto dmask = [&](float (&ds)[16], int kt) {
+        if (diag) {
           asm volatile("" ::: "memory");
-          // this lane's query less the key offset 4 hl, from a fresh lane id
-          // (no register is held across the tile loop for it)
           const int fl = sa::fresh_lane();
           const int qd = 32 * w + (fl & 31) - 4 * (fl >> 5) - ksub - 32 * kt;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (8 * (r >> 2) + (r & 3) > qd) ds[r] = 0.f;
         }
-        const sa::u32x4 bo[2] = {pack8(ds), pack8(ds + 8)};
-        crd(std::integral_constant<int, RC>{});  // RC + 1 ahead from here on
-        // dQ^T [d x queries] += K^T [d x keys] dS^T [keys x queries]
-        sa::static_for<0, NC>([&](auto jj) {
-          constexpr int J = decltype(jj)::value;
-          SA_SCHED_BARRIER();
-          acc[J % NT] = sa::mfma32(cbuf[J], bo[J / NT], acc[J % NT]);
-          crd(std::integral_constant<int, J + RC + 1>{});
-        });
-        SA_SCHED_BARRIER();
       };
-      bwd_tile<D>(diag, half);
+      sa::f32x16 s0, dp0, s1, dp1;
+      float ds0[16], ds1[16];
+      // S^T, dP^T of half 0
+      sa::static_for<0, RA>([&](auto m) { ard(H0{}, m); });
+      sa::static_for<0, NA>([&](auto m) {
+        constexpr int Mi = decltype(m)::value;
+        SA_SCHED_BARRIER();
+        sdp_mfma(H0{}, m, s0, dp0);
+        ard(H0{}, std::integral_constant<int, Mi + RA>{});
+      });
+      SA_SCHED_BARRIER();
+      // S^T, dP^T of half 1 beside dS^T of half 0
+      sa::static_for<0, RA>([&](auto m) { ard(H1{}, m); });
+      SA_SCHED_BARRIER();
+      sa::static_for<0, NA>([&](auto m) {
+        constexpr int Mi = decltype(m)::value;
+        sdp_mfma(H1{}, m, s1, dp1);
+        ard(H1{}, std::integral_constant<int, Mi + RA>{});
+      });
+      dsoft(s0, dp0, ds0);
+      sa::static_for<0, NA>([&](auto m) {
+        constexpr int Mi = decltype(m)::value;
+        SA_SCHED_GROUP(0x008, 1);
+        if constexpr (Mi + RA < NA) SA_SCHED_GROUP(0x100, 1);
+        SA_SCHED_GROUP(0x002, 64 / NA);
+      });
+      SA_SCHED_GROUP(0x002, 64);
+      SA_SCHED_BARRIER();
+      dmask(ds0, 0);
+      const sa::u32x4 bo0[2] = {pack8(ds0), pack8(ds0 + 8)};
+      // dQ^T of half 0 beside dS^T of half 1
+      sa::static_for<0, RC>([&](auto j) { crd(H0{}, j); });
+      SA_SCHED_BARRIER();
+      sa::static_for<0, NC>([&](auto jj) {
+        constexpr int J = decltype(jj)::value;
+        acc[J % NT] = sa::mfma32(cbuf[0][J], bo0[J / NT], acc[J % NT]);
+        crd(H0{}, std::integral_constant<int, J + RC>{});
+      });
+      dsoft(s1, dp1, ds1);
+      sa::static_for<0, NC>([&](auto jj) {
+        constexpr int J = decltype(jj)::value;
+        SA_SCHED_GROUP(0x008, 1);
+        if constexpr (J + RC < NC) SA_SCHED_GROUP(0x100, 2);
+        SA_SCHED_GROUP(0x002, 64 / NC);
+      });
+      SA_SCHED_GROUP(0x002, 64);
+      SA_SCHED_BARRIER();
+      dmask(ds1, 1);
+      const sa::u32x4 bo1[2] = {pack8(ds1), pack8(ds1 + 8)};
+      // dQ^T of half 1
+      sa::static_for<0, RC>([&](auto j) { crd(H1{}, j); });
+      sa::static_for<0, NC>([&](auto jj) {
+        constexpr int J = decltype(jj)::value;
+        SA_SCHED_BARRIER();
+        acc[J % NT] = sa::mfma32(cbuf[1][J], bo1[J / NT], acc[J % NT]);
+        crd(H1{}, std::integral_constant<int, J + RC>{});
+      });
+      SA_SCHED_BARRIER();
     }
   }
   // C rows of tile dt are d = 32 dt + 8(r/4) + 4(l/32) + r%4 of this lane's query
