@@ -405,10 +405,17 @@ sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, con
  *                    sparse_attn_bwd_workspace_bytes(B, H, H_kv, N, d, block)
  *                    (else SA_ERR_CAPACITY): per-row {lse log2(e), D}, the
  *                    dK/dV work list, and fp32 partial dK/dV of key blocks
- *                    listed by more than 64 query blocks (32 at block 128);
- *                    those are split over several workgroups and their
- *                    partial sums added with fp32 atomics, so their low-order
- *                    bits may differ from run to run
+ *                    listed by more than 16 (query block, q head) pairs of
+ *                    their K/V head; those are split over several workgroups
+ *                    and their partial sums added with fp32 atomics, so their
+ *                    low-order bits may differ from run to run
+ *   sched            DEVICE int32 [num_groups][N_b] or NULL: the launch order
+ *                    of the dQ rows, as for sparse_attn_fwd (the
+ *                    longest-first order of sparse_attn_build_mask shortens
+ *                    the tail when a few rows are much longer than the rest);
+ *                    each group's list must be a permutation of 0 .. N_b - 1
+ *                    (a row id outside [0, N_b) leaves a dQ block unwritten).
+ *                    Results do not depend on it; the fp32 path ignores it.
  *   strides          HOST int64 [8][3] for q, k, v, o, dout, dq, dk, dv
  *                    (batch, head, sequence strides in elements) or NULL; for
  *                    bf16 the sequence strides of q, k, v, dout must be below
@@ -422,8 +429,9 @@ sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k, const voi
                           int64_t workspace_bytes, int32_t B, int32_t H, int32_t H_kv, int32_t N, int32_t d,
                           int32_t block,
                           const int64_t* strides, const int32_t* row_ptr, const int32_t* col_idx,
-                          int64_t col_capacity, const int32_t* col_ptr, const int32_t* row_idx,
-                          int64_t row_capacity, int32_t num_groups, int64_t mask_batch_stride,
+                          int64_t col_capacity, const int32_t* sched, const int32_t* col_ptr,
+                          const int32_t* row_idx, int64_t row_capacity, int32_t num_groups,
+                          int64_t mask_batch_stride,
                           int64_t mask_head_stride, int32_t causal, float scale, hipStream_t stream);
 
 /*

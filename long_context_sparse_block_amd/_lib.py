@@ -94,8 +94,8 @@ SIGNATURES = {
     "sparse_attn_mask_transpose": (_i32, [_i32, _i32, _p, _p, _i64, _p, _p, _i64, _p]),
     "sparse_attn_bwd_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sparse_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i32, _i32, _i32,
-                               ctypes.POINTER(_i64), _p, _p, _i64, _p, _p, _i64, _i32, _i64, _i64, _i32, _f32,
-                               _p]),
+                               ctypes.POINTER(_i64), _p, _p, _i64, _p, _p, _p, _i64, _i32, _i64, _i64, _i32,
+                               _f32, _p]),
     "offset_attn_bwd": (_i32, [_i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                ctypes.POINTER(_i64), ctypes.POINTER(_i32), _i32, _f32, _p]),
     "sa_rng_key": (_u64, [_u64, _u64, _u64, _u64, _u64]),

@@ -322,9 +322,11 @@ def _bwd_workspace(B, H, Hkv, N, d, block, device):
 
 
 def sparse_attn_bwd(q, k, v, o, lse, dout, mask, transpose=None, scale=None, mask_batch_stride=0,
-                    mask_head_stride=0):
+                    mask_head_stride=0, use_schedule=True):
     """Gradients (dq, dk, dv) of block-sparse attention; ``transpose`` is the
-    result of sparse_attn_mask_transpose(mask) (computed when omitted)."""
+    result of sparse_attn_mask_transpose(mask) (computed when omitted); the
+    dQ rows run in the mask's launch order when it has one and
+    ``use_schedule``."""
     B, H, Hkv, N, d = _check_qkv(q, k, v)
     block = N // mask.num_blocks
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -334,8 +336,9 @@ def sparse_attn_bwd(q, k, v, o, lse, dout, mask, transpose=None, scale=None, mas
     st = L.lib().sparse_attn_bwd(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(ws), ws.numel(), B, H, Hkv, N, d, block, _strides(q, k, v, o, dout, dq, dk, dv), _ptr(mask.row_ptr),
-        _ptr(mask.col_idx), mask.col_idx.numel(), _ptr(col_ptr), _ptr(row_idx), row_idx.numel(),
-        mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal), scale, _stream(q.device))
+        _ptr(mask.col_idx), mask.col_idx.numel(), _ptr(mask.sched if use_schedule else None), _ptr(col_ptr),
+        _ptr(row_idx), row_idx.numel(), mask.num_groups, mask_batch_stride, mask_head_stride, int(mask.causal),
+        scale, _stream(q.device))
     _check(st, "sparse_attn_bwd")
     return dq, dk, dv
 
@@ -579,7 +582,8 @@ class BlockSparseBwdPlan:
         self._args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(plan.o), _ptr(plan.lse), _ptr(dout),
                       _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.ws), self.ws.numel(), B, H, Hkv, N, d,
                       N // m.num_blocks, _strides(q, k, v, plan.o, dout, self.dq, self.dk, self.dv),
-                      _ptr(m.row_ptr), _ptr(m.col_idx), m.col_idx.numel(), _ptr(self.col_ptr), _ptr(self.row_idx),
+                      _ptr(m.row_ptr), _ptr(m.col_idx), m.col_idx.numel(), _ptr(m.sched), _ptr(self.col_ptr),
+                      _ptr(self.row_idx),
                       self.row_idx.numel(), m.num_groups, plan.mbs, plan.mhs, int(m.causal), plan.scale)
         self.transpose()
 

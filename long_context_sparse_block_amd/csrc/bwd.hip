@@ -49,6 +49,7 @@ struct BwdArgs {
   const int32_t* col_idx;
   const int32_t* col_ptr;
   const int32_t* row_idx;
+  const int32_t* sched;  // per group, the rows in launch order (or NULL: ascending)
   int64_t col_capacity, row_capacity;
   int32_t B, H, H_kv, N, nb, G;
   int64_t mbs, mhs;
@@ -504,9 +505,16 @@ __global__ __launch_bounds__(2 * BLK) void bsa_bwd_dq_bf16(BwdArgs a) {
   static_assert(S == 2 || S == 3, "ring slots");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = sa::uniform(tid >> 6), hl = lane >> 5;
-  const int32_t bh = blockIdx.x / a.nb, i = blockIdx.x % a.nb;
+  // blockIdx = pos * (B * H) + bh: with B * H a multiple of 8 every query
+  // block of one head runs on the same XCD (the key blocks that neighbouring
+  // query blocks share stay in one L2); pos is a launch position of the
+  // head's mask group, longest row first when `sched` is given
+  const int32_t BH = a.B * a.H;
+  const int32_t bh = blockIdx.x % BH, pos = blockIdx.x / BH;
   const int32_t b = bh / a.H, h = bh % a.H, kvh = h / (a.H / a.H_kv);
   const int64_t g = (int64_t)b * a.mbs + (int64_t)h * a.mhs;
+  const int32_t i = sa::uniform(a.sched ? a.sched[g * a.nb + pos] : pos);
+  if (i < 0 || i >= a.nb) return;
   const int qoff = 32 * w + (lane & 31);           // this lane's query inside the block
   const int64_t tq = (int64_t)i * BLK + qoff;      // ... and in the sequence (C column)
   const uint16_t* Q = (const uint16_t*)a.q + b * a.st[TQ][0] + h * a.st[TQ][1];
@@ -823,7 +831,11 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
     int64_t c;
     int32_t chunk;
     if (item >= extra) {
-      c = item - extra;
+      // first chunks in (j, bk) order: consecutive items take the same key
+      // block of different heads, so (B * H_kv a multiple of 8) every key
+      // block of one head runs on the same XCD, like its query blocks
+      const int32_t x = item - extra, bhk = a.B * a.H_kv;
+      c = (int64_t)(x % bhk) * a.nb + x / bhk;
       chunk = 0;
     } else {
       // pre[c] - c counts the extra chunks of the columns before c: the item's
@@ -1457,7 +1469,8 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
                                      void* workspace, int64_t workspace_bytes, int32_t B, int32_t H,
                                      int32_t H_kv, int32_t N, int32_t d,
                                      int32_t block, const int64_t* strides, const int32_t* row_ptr,
-                                     const int32_t* col_idx, int64_t col_capacity, const int32_t* col_ptr,
+                                     const int32_t* col_idx, int64_t col_capacity, const int32_t* sched,
+                                     const int32_t* col_ptr,
                                      const int32_t* row_idx, int64_t row_capacity, int32_t num_groups,
                                      int64_t mask_batch_stride, int64_t mask_head_stride, int32_t causal,
                                      float scale, hipStream_t stream) {
@@ -1485,7 +1498,7 @@ extern "C" sa_status sparse_attn_bwd(int32_t dtype, const void* q, const void* k
   if (dtype == SA_BF16)
     for (int t : {(int)TQ, (int)TK, (int)TV, (int)TDO})
       if (a.st[t][2] >= (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
-  a.row_ptr = row_ptr, a.col_idx = col_idx, a.col_ptr = col_ptr, a.row_idx = row_idx;
+  a.row_ptr = row_ptr, a.col_idx = col_idx, a.col_ptr = col_ptr, a.row_idx = row_idx, a.sched = sched;
   a.col_capacity = col_capacity, a.row_capacity = row_capacity;
   a.nb = N / block, a.G = num_groups, a.mbs = mask_batch_stride, a.mhs = mask_head_stride, a.causal = causal;
   const bool bf = dtype == SA_BF16;

@@ -287,7 +287,7 @@ def _bwd(lib, **kw):
     a.update(kw)
     return lib.sparse_attn_bwd(a["dtype"], fake, fake, fake, fake, fake, fake, fake, fake, fake, a["ws"],
                                a["ws_bytes"], a["B"], a["H"], a["H_kv"], a["N"], a["d"], a["block"],
-                               a["strides"], fake, fake, 100, fake, fake, 100, a["G"], a["mbs"], a["mhs"],
+                               a["strides"], fake, fake, 100, None, fake, fake, 100, a["G"], a["mbs"], a["mhs"],
                                a["causal"], a["scale"], None)
 
 
