@@ -470,8 +470,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernel",
-                    choices=sorted(wl.BLOCK_WORKLOADS) + ["offsets-2048", "offsets-8192", "long-context-bwd",
-                                                          "compression-guided-bwd"],
+                    choices=sorted(wl.BLOCK_WORKLOADS) + ["offsets-2048", "offsets-8192"]
+                    + [n + "-bwd" for n in sorted(wl.BLOCK_WORKLOADS) if wl.BLOCK_WORKLOADS[n]["dtype"] == wl.BF16],
                     help="run only the given workload's kernels (for counter collection), then exit")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="run a plain device copy of MIB MiB (traffic-counter calibration), then exit")

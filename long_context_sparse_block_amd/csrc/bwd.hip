@@ -753,31 +753,36 @@ __global__ __launch_bounds__(256) void dkdv_plan_kernel(BwdArgs a) {
   }
 }
 
-// One wave per split column: fp32 partial sums -> bf16 dk (scaled), dv.
+// Split columns: fp32 partial sums -> bf16 dk (scaled), dv; kConvWaves waves
+// per column, each converting 512 consecutive floats of dK and of dV (8 per
+// lane, lanes along the row), so that all of the partials are in flight at once.
+template <int D, int BLK>
+constexpr int kConvWaves = BLK * D / 512;
+
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void dkdv_convert_kernel(BwdArgs a) {
+  constexpr int WPC = kConvWaves<D, BLK>;
   const int lane = threadIdx.x & 63;
-  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
+  const int64_t c = wv / WPC;
   if (c >= cols || a.pre[c + 1] - a.pre[c] <= 1) return;
   const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
   const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
   const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
-  const float* r0 = a.acc + ((int64_t)bk * a.N + (int64_t)j * BLK) * D;
-  for (int x = lane; x < BLK * D / 8; x += 64) {
-    const int r = x / (D / 8), c8 = x % (D / 8);
-    const int64_t key = (int64_t)j * BLK + r;
-    const float* pk = r0 + r * D + 8 * c8;
-    const float* pv = pk + plane;
-    sa::u32x4 wk, wv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wk[e] = sa::pack_bf16x2(pk[2 * e] * a.scale, pk[2 * e + 1] * a.scale);
-      wv[e] = sa::pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
-    }
-    *(sa::u32x4*)((uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + key * a.st[TDK][2] + 8 * c8) = wk;
-    *(sa::u32x4*)((uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + key * a.st[TDV][2] + 8 * c8) = wv;
-  }
+  const int x = (int)(wv % WPC) * 64 + lane;  // 8-float group of the column
+  const int r = x / (D / 8), c8 = x % (D / 8);
+  const float* pk = a.acc + ((int64_t)bk * a.N + (int64_t)j * BLK + r) * D + 8 * c8;
+  const float* pv = pk + plane;
+  const sa::f32x4 k0 = *(const sa::f32x4*)pk, k1 = *(const sa::f32x4*)(pk + 4);
+  const sa::f32x4 v0 = *(const sa::f32x4*)pv, v1 = *(const sa::f32x4*)(pv + 4);
+  const int64_t key = (int64_t)j * BLK + r;
+  *(sa::u32x4*)((uint16_t*)a.dk + b * a.st[TDK][0] + kvh * a.st[TDK][1] + key * a.st[TDK][2] + 8 * c8) =
+      sa::u32x4{sa::pack_bf16x2(k0[0] * a.scale, k0[1] * a.scale), sa::pack_bf16x2(k0[2] * a.scale, k0[3] * a.scale),
+                sa::pack_bf16x2(k1[0] * a.scale, k1[1] * a.scale), sa::pack_bf16x2(k1[2] * a.scale, k1[3] * a.scale)};
+  *(sa::u32x4*)((uint16_t*)a.dv + b * a.st[TDV][0] + kvh * a.st[TDV][1] + key * a.st[TDV][2] + 8 * c8) =
+      sa::u32x4{sa::pack_bf16x2(v0[0], v0[1]), sa::pack_bf16x2(v0[2], v0[3]), sa::pack_bf16x2(v1[0], v1[1]),
+                sa::pack_bf16x2(v1[2], v1[3])};
 }
 
 // dk, dv: persistent workgroups (BLK/32 waves, one per 32 keys of the key
@@ -1413,7 +1418,8 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     st = launch(bsa_bwd_dkdv_bf16<D, BLK, SK, VL>, a, std::min<int64_t>(nk + nk / 2 + 64, 8192), 2 * BLK, lds_kv,
                 stream, "bsa_bwd_dkdv_bf16");
     if (st != SA_OK) return st;
-    return launch(dkdv_convert_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_convert_kernel");
+    return launch(dkdv_convert_kernel<D, BLK>, a, (nk * kConvWaves<D, BLK> + 3) / 4, 256, 0, stream,
+                  "dkdv_convert_kernel");
   }
   st = launch(bsa_bwd_dq_f32<D, BLK>, a, nq, BLK, 0, stream, "bsa_bwd_dq_f32");
   if (st != SA_OK) return st;
