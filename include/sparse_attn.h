@@ -405,10 +405,12 @@ sa_status sparse_attn_mask_transpose(int32_t num_groups, int32_t num_blocks, con
  *                    sparse_attn_bwd_workspace_bytes(B, H, H_kv, N, d, block)
  *                    (else SA_ERR_CAPACITY): per-row {lse log2(e), D}, the
  *                    dK/dV work list, and fp32 partial dK/dV of key blocks
- *                    listed by more than 16 (query block, q head) pairs of
- *                    their K/V head; those are split over several workgroups
- *                    and their partial sums added with fp32 atomics, so their
- *                    low-order bits may differ from run to run
+ *                    listed by more than L (query block, q head) pairs of
+ *                    their K/V head, L = the mask's entries per resident
+ *                    dK/dV workgroup, clamped to 16 .. 64; those are split
+ *                    over several workgroups and their partial sums added
+ *                    with fp32 atomics, so their low-order bits may differ
+ *                    from run to run
  *   sched            DEVICE int32 [num_groups][N_b] or NULL: the launch order
  *                    of the dQ rows, as for sparse_attn_fwd (the
  *                    longest-first order of sparse_attn_build_mask shortens

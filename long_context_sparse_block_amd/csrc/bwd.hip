@@ -24,6 +24,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <type_traits>
 
 #include "sa_device.h"
@@ -61,7 +64,8 @@ struct BwdArgs {
   // `chunk` entries; pre[c] = first work item of column c (exclusive scan)
   int32_t* pre;
   float* acc;  // fp32 [2][B][H_kv][N][d]: partial dK, dV of split columns
-  int32_t chunk;
+  int32_t chunk;  // least entries per chunk
+  int64_t slots;  // dK/dV workgroups resident on the GPU at once
 };
 
 enum { TQ = 0, TK = 1, TV = 2, TO = 3, TDO = 4, TDQ = 5, TDK = 6, TDV = 7 };
@@ -731,8 +735,31 @@ __device__ __forceinline__ int32_t column_len(const BwdArgs& a, int32_t b, int32
   return n;
 }
 
-// One wave per column: pre[c + 1] = number of work items (chunks) of column c;
-// a column split in several chunks gets its fp32 partial rows zeroed.
+// Entries per dK/dV work item: the entries of all columns spread over the
+// resident workgroups, at least a.chunk and at most 64 (an item's list is held
+// in VGPR lanes).  Columns longer than that are split in chunks, whose fp32
+// partials are added atomically; shorter ones are one item each.  The same
+// value in every wave (a sum over the heads' mask groups).
+__device__ __forceinline__ int32_t chunk_entries(const BwdArgs& a, int lane) {
+  int64_t tot = 0;
+  for (int64_t x = lane; x < (int64_t)a.B * a.H; x += 64) {
+    const int64_t g = (x / a.H) * a.mbs + (x % a.H) * a.mhs;
+    int64_t e0 = a.col_ptr[g * a.nb], e1 = a.col_ptr[g * a.nb + a.nb];
+    e0 = max((int64_t)0, min(e0, a.row_capacity));
+    e1 = max(e0, min(e1, a.row_capacity));
+    tot += e1 - e0;
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int lo = __shfl_xor((int)(uint32_t)tot, m), hi = __shfl_xor((int)(tot >> 32), m);
+    tot += ((int64_t)hi << 32) | (uint32_t)lo;
+  }
+  const int64_t per = (tot + a.slots - 1) / a.slots;
+  return (int32_t)max((int64_t)a.chunk, min(per, (int64_t)64));
+}
+
+// One wave per column: pre[c + 1] = number of work items (chunks) of column c,
+// pre[cols + 1] = entries per chunk; a column split in several chunks gets its
+// fp32 partial rows zeroed.
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void dkdv_plan_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
@@ -741,8 +768,10 @@ __global__ __launch_bounds__(256) void dkdv_plan_kernel(BwdArgs a) {
   if (c >= cols) return;
   const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
   const int32_t len = column_len(a, bk / a.H_kv, bk % a.H_kv, j);
-  const int32_t chunks = max(1, (len + a.chunk - 1) / a.chunk);
+  const int32_t L = chunk_entries(a, lane);
+  const int32_t chunks = max(1, (len + L - 1) / L);
   if (lane == 0) a.pre[c + 1] = chunks;
+  if (c == 0 && lane == 0) a.pre[cols + 1] = L;
   if (chunks > 1) {
     const int64_t plane = (int64_t)a.B * a.H_kv * a.N * D;
     float* r0 = a.acc + ((int64_t)bk * a.N + (int64_t)j * BLK) * D;
@@ -820,6 +849,7 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
   const int32_t rep = a.H / a.H_kv;
   const int64_t cols = (int64_t)a.B * a.H_kv * a.nb;
   const int32_t items = a.pre[cols];
+  const int32_t chunkL = sa::uniform(a.pre[cols + 1]);  // entries per chunk, 16 .. 64
   // Items [0, extra) are the second and later chunks of split columns (the
   // long ones, started first); item extra + c is the first chunk of column c.
   const int32_t extra = items - (int32_t)cols;
@@ -861,7 +891,7 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
     const int split = sa::uniform((int)(a.pre[c + 1] - a.pre[c] > 1));
     const int32_t bk = (int32_t)(c / a.nb), j = (int32_t)(c % a.nb);
     const int32_t b = bk / a.H_kv, kvh = bk % a.H_kv;
-    const int32_t f0 = chunk * a.chunk;  // first flat entry of this item
+    const int32_t f0 = chunk * chunkL;  // first flat entry of this item
     const int koff = 32 * kg + (lane & 31);       // this lane's key inside the block
     const int64_t sk = (int64_t)j * BLK + koff;   // ... and in the sequence (C column)
     const uint16_t* K = (const uint16_t*)a.k + b * a.st[TK][0] + kvh * a.st[TK][1];
@@ -878,14 +908,14 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
       int32_t e0, e1;
       col_range(a, (int64_t)b * a.mbs + (int64_t)h * a.mhs, j, e0, e1);
       const int32_t x = f0 + lane - total;
-      if (lane < a.chunk && x >= 0 && x < e1 - e0) {
+      if (lane < chunkL && x >= 0 && x < e1 - e0) {
         const int32_t qb = a.row_idx[e0 + x];
         lq = ((uint32_t)qb < (uint32_t)a.nb && !(a.causal && qb < j)) ? qb : -1;
         lh = h;
       }
       total += e1 - e0;
     }
-    const int cnt = sa::uniform(max(0, min(a.chunk, total - f0)));
+    const int cnt = sa::uniform(max(0, min(chunkL, total - f0)));
     // the loads above complete here, before any copy is in flight (stores of
     // the previous item included)
 #pragma unroll
@@ -1387,11 +1417,28 @@ sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t s
                  : launch(delta_kernel<128, false>, a, blocks, 256, 0, stream, "delta_kernel");
 }
 
-// CSR entries per dK/dV work item: longer columns are split over several
-// workgroups (an item's list, at most 64 entries, is held in VGPR lanes).
-// 16 measured best at block 64 and 128 (8, 32 and 64 were slower on one of
-// the two block sizes or both).
+// Least CSR entries per dK/dV work item (chunks grow up to 64 entries when
+// the columns' entries outnumber the resident workgroups).
 constexpr int kChunkEntries = 16;
+
+// Workgroups of `kern` resident on the current device at once (cached per
+// device and kernel).
+int64_t resident_workgroups(const void* kern, int threads, int lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kern);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  (void)hipGetLastError();
+  return cache[key] = (int64_t)per_cu * cus;
+}
 
 
 template <int D, int BLK>
@@ -1409,7 +1456,11 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
     st = launch(bsa_bwd_dq_bf16<D, BLK, SQ>, a, nq, 2 * BLK, lds_dq, stream, "bsa_bwd_dq_bf16");
     if (st != SA_OK) return st;
     const int64_t wblocks = (nk + 3) / 4;
-    st = launch(dkdv_plan_kernel<D, BLK>, a, wblocks, 256, 0, stream, "dkdv_plan_kernel");
+    const sa_status ls = allow_lds((const void*)bsa_bwd_dkdv_bf16<D, BLK, SK, VL>, lds_kv);
+    if (ls != SA_OK) return ls;
+    BwdArgs ap = a;
+    ap.slots = resident_workgroups((const void*)bsa_bwd_dkdv_bf16<D, BLK, SK, VL>, 2 * BLK, lds_kv);
+    st = launch(dkdv_plan_kernel<D, BLK>, ap, wblocks, 256, 0, stream, "dkdv_plan_kernel");
     if (st != SA_OK) return st;
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.pre, nk);
     st = sa_host::check_launch("scan_kernel");
@@ -1427,7 +1478,7 @@ sa_status launch_bsa_bwd(const BwdArgs& a, bool bf16, hipStream_t stream) {
 }
 
 // Workspace of sparse_attn_bwd: row statistics fp32 [B*H*N][2] ({lse log2(e),
-// D} pairs; D alone in the first half for fp32) | pre int32 [B*H_kv*nb + 1] |
+// D} pairs; D alone in the first half for fp32) | pre int32 [B*H_kv*nb + 2] |
 // acc fp32 [2][B*H_kv*N*d], each part 256-byte aligned.
 struct WsLayout {
   int64_t stat, pre, acc, total;
@@ -1437,7 +1488,7 @@ WsLayout ws_layout(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int
   WsLayout l;
   l.stat = 0;
   l.pre = up(B * H * N * 8);
-  l.acc = l.pre + up((B * H_kv * (N / block) + 1) * 4);
+  l.acc = l.pre + up((B * H_kv * (N / block) + 2) * 4);
   l.total = l.acc + up(2 * B * H_kv * N * d * 4);
   return l;
 }

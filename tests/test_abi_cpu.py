@@ -317,10 +317,11 @@ def test_bwd_host_errors(lib, over, status):
 
 
 def test_bwd_workspace_bytes(lib):
-    # {lse log2(e), D} per row | work-item prefix | fp32 partial dK, dV; parts 256-byte aligned
+    # {lse log2(e), D} per row | work-item prefix and chunk size | fp32 partial dK, dV;
+    # parts 256-byte aligned
     up = lambda x: (x + 255) // 256 * 256
     for B, H, Hkv, N, d, blk in ((1, 2, 2, 512, 64, 64), (2, 8, 2, 4096, 128, 128), (3, 3, 1, 192, 64, 64)):
-        want = up(8 * B * H * N) + up(4 * (B * Hkv * (N // blk) + 1)) + up(2 * 4 * B * Hkv * N * d)
+        want = up(8 * B * H * N) + up(4 * (B * Hkv * (N // blk) + 2)) + up(2 * 4 * B * Hkv * N * d)
         assert lib.sparse_attn_bwd_workspace_bytes(B, H, Hkv, N, d, blk) == want
     assert lib.sparse_attn_bwd_workspace_bytes(0, 1, 1, 64, 64, 64) < 0
 
