@@ -467,31 +467,14 @@ __device__ __forceinline__ sa::u32x4 pack8(const float* x) {
                    sa::pack_bf16x2(x[6], x[7])};
 }
 
-// The two 32-row halves of a 64-row tile.  With SPLIT the diagonal (causal)
-// tile runs a variant of its own and the others skip the mask; with ILV both
-// halves sit in one basic block so that their MFMAs and VALU work interleave
-// (more registers).
-// d = 64: the diagonal tile has a variant of its own; d = 128: one masked
-// variant (two would keep twice the operand addresses live).
-template <int D>
-struct TileCfg {
-  static constexpr bool SPLIT = D == 64;
-};
-template <int D, typename F>
-__device__ __forceinline__ void bwd_tile(bool diag, F& half) {
-  constexpr bool SPLIT = TileCfg<D>::SPLIT;
-  auto run = [&](auto mask_tag) {
+// The two 32-row halves of a 64-row tile, one loop body: the causal mask of
+// the diagonal tile is a wave-uniform branch inside it.  (A second copy of
+// the loop for the diagonal tile made the compiler move the dK / dV
+// accumulators between register sets around it on every tile.)
+template <typename F>
+__device__ __forceinline__ void bwd_tile(F& half) {
 #pragma unroll 1
-    for (int x = 0; x < 2; ++x) half(x, mask_tag);
-  };
-  if constexpr (SPLIT) {
-    if (diag)
-      run(std::true_type{});
-    else
-      run(std::false_type{});
-  } else {
-    run(std::true_type{});
-  }
+  for (int x = 0; x < 2; ++x) half(x);
 }
 
 // dq: one workgroup (BLK/32 waves) per query block, a wave per 32 queries.  The
@@ -976,9 +959,8 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
         const float* sts = (const float*)(gs + M::TB);
         const int qsub = 64 * (n % SUBS);
         const bool diag = a.causal && qb == j;
-        // one 32-query half; MASK: apply the causal triangle when diag
-        auto half = [&](int qt, auto mask_tag) {
-          constexpr bool MASK = decltype(mask_tag)::value;
+        // one 32-query half; the causal triangle applies when diag
+        auto half = [&](int qt) {
           // V rows of this wave's keys, read again for every half (the opaque
           // base keeps the compiler from holding them in registers)
           uint32_t vrows = vblk + (uint32_t)(32 * kg / 64) * M::TB;
@@ -1043,7 +1025,7 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
               ds[r] = p[r] * (dp[r] - dv4[cc]);
             }
           }
-          if (MASK && diag) {
+          if (diag) {
             // keys after the query (diagonal tile only: a wave-uniform branch,
             // kept as one by the volatile asm, so other tiles skip the selects)
             asm volatile("" ::: "memory");
@@ -1067,7 +1049,7 @@ void bsa_bwd_dkdv_bf16(BwdArgs a) {
           });
           SA_SCHED_BARRIER();
         };
-        bwd_tile<D>(diag, half);
+        bwd_tile(half);
       }
       if constexpr (S == 1) {
         if (n + 1 < T) {
