@@ -156,6 +156,35 @@ class ClockProbe:
         return round(cyc / ticks * WALL_CLOCK_MHZ, 1) if ticks > 0 else None
 
 
+def gemm_reference(n=8192, iters=50):
+    """Dense bf16 GEMM rate of the vendor library (torch.matmul -> hipBLASLt)
+    on this GPU, with iid N(0, 1) operands (the distribution of every workload
+    here) and with all-ones operands.  The same GEMM runs markedly faster on
+    constant operands, so the random-data rate is the practical ceiling that
+    random-data MFMA work meets on this GPU; it is context for the roofline
+    fractions, not part of the attention path."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    out = {"n": n}
+    for name, mk in (("normal", lambda: torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)),
+                     ("ones", lambda: torch.ones(n, n, device="cuda", dtype=torch.bfloat16))):
+        a, b = mk(), mk().t().contiguous().t()  # B column-major: the library's faster layout here
+        for _ in range(5):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[f"tflops_{name}"] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b
+    out["frac_of_peak_normal"] = round(out["tflops_normal"] / PEAK_BF16_TFLOPS, 3)
+    torch.cuda.empty_cache()
+    return out
+
+
 # -------------------------------------------------------- oracle baselines --
 
 def _sample_rows(rp, nb, G, stride):
@@ -541,7 +570,8 @@ def main():
                    "kernel_trials": args.trials, "kernel_stat": "median"},
         "roofline": roofline_mfma(head["flops"], head["fwd_ms"], fwd_kernel_name(w),
                                   traffic=(traffic or {}).get("bytes_per_launch")),
-        "system": {"shader_clock_mhz_measured": clock, "device": torch.cuda.get_device_name(0), "host": HOST},
+        "system": {"shader_clock_mhz_measured": clock, "device": torch.cuda.get_device_name(0), "host": HOST,
+                   "dense_bf16_gemm_reference": gemm_reference()},
     }
     if cpu:
         out["cpu_baseline"] = cpu_line(cpu_block_forward, head, 12.0)
