@@ -1404,21 +1404,27 @@ sa_status launch_delta(const BwdArgs& a, int32_t dtype, int32_t d, hipStream_t s
 constexpr int kChunkEntries = 16;
 
 // Workgroups of `kern` resident on the current device at once (cached per
-// device and kernel).
+// device and kernel).  The value only sizes the dK/dV work items, so a failed
+// query falls back to one workgroup per CU of a 256-CU device (and its error
+// is cleared here rather than left for the caller's next HIP call).
 int64_t resident_workgroups(const void* kern, int threads, int lds) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int64_t> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
   std::lock_guard<std::mutex> lock(mu);
   const auto key = std::make_pair(dev, kern);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  (void)hipGetLastError();
+  const hipError_t e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
+  const hipError_t e2 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e1 != hipSuccess || e2 != hipSuccess) (void)hipGetLastError();
+  if (e1 != hipSuccess || per_cu < 1) per_cu = 1;
+  if (e2 != hipSuccess || cus < 1) cus = 256;
   return cache[key] = (int64_t)per_cu * cus;
 }
 
