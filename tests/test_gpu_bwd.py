@@ -351,8 +351,8 @@ def test_bsa_bwd_long_context_full_size_sampled_heads():
     """The long-context workload at full size ([1, 16, 65536, 128], block 128),
     run as the bench runs it; whole heads 0 and 15 checked against the oracle.
     19 of its 512 rows list 65 to 83 key blocks (a second dQ pass) and the four
-    global key blocks are listed by every later query block (32 dK / dV work
-    items each)."""
+    global key blocks are listed by every later query block (split over eight
+    dK / dV work items each: this size gets 64 entries per item)."""
     require_gpu()
     w = wl.BLOCK_WORKLOADS["long-context"]
     spec = workload_spec(w)
@@ -373,3 +373,31 @@ def test_bsa_bwd_long_context_full_size_sampled_heads():
     qs, ks, vs, ds = [f64(t[:, sel]) for t in (q, k, v, do)]
     ref = ob.csr_attention_bwd(qs, ks, vs, ds, rp, ci, w["block"], True, scale, mags=True)
     _check_all(got, ref, torch.bfloat16, "long-context full size")
+
+
+def test_bsa_bwd_bigbird_full_size_sampled_heads():
+    """The BigBird workload at full size ([2, 12, 4096, 64], non-causal, block
+    64), run as the bench runs it: the two global key blocks are listed by all
+    64 query blocks of a head, so their columns are split over four dK / dV
+    work items (16 entries each at this size) whose fp32 partials meet in the
+    workspace; three whole (batch, head) slices checked against the oracle."""
+    require_gpu()
+    w = wl.BLOCK_WORKLOADS["bigbird"]
+    spec = workload_spec(w)
+    rp, ci, _ = bm.build(spec)
+    assert spec["mask_batch_stride"] == 0 and spec["mask_head_stride"] == 0  # one mask for every head
+    heads = [(0, 0), (1, 5), (w["B"] - 1, w["H"] - 1)]
+    announce(f"[bwd] bigbird full size {w['B']}x{w['H']}x{w['N']}x{w['d']}, heads {heads}")
+    q, k, v = wl.make_qkv(w["B"], w["H"], w["N"], w["d"], torch.bfloat16, w["qkv_seed"])
+    do = _dout(q.shape, torch.bfloat16, w["qkv_seed"] + 1)
+    plan = api.BlockSparsePlan(spec, q.cuda(), k.cuda(), v.cuda())
+    plan()
+    bp = api.BlockSparseBwdPlan(plan, do.cuda())
+    got = bp()
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.mask.row_ptr.cpu().numpy(), rp)
+    scale = 1.0 / math.sqrt(w["d"])
+    got = [torch.stack([t[b, h] for b, h in heads])[None] for t in got]
+    qs, ks, vs, ds = [f64(torch.stack([t[b, h] for b, h in heads])[None]) for t in (q, k, v, do)]
+    ref = ob.csr_attention_bwd(qs, ks, vs, ds, rp, ci, w["block"], False, scale, mags=True)
+    _check_all(got, ref, torch.bfloat16, "bigbird full size")
